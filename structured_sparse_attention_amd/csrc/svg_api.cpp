@@ -1,0 +1,346 @@
+// Host side of the C ABI: argument validation, tile-map lifecycle, kernel
+// dispatch and error reporting. Every entry point validates its arguments
+// before the first HIP call and reports failures as svg_status values with a
+// thread-local message; nothing throws across the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "svg_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+svg_status fail(svg_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+svg_status ok() {
+  g_last_error.clear();
+  return SVG_OK;
+}
+
+svg_status hip_fail(hipError_t e, const char* what) {
+  return fail(SVG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool tile_q_ok(int32_t bq) {
+  return bq == 32 || bq == 64 || bq == 128 || (bq >= 256 && bq <= (1 << 20) && bq % 256 == 0);
+}
+bool tile_k_ok(int32_t bk) { return bk >= 32 && bk <= 1024 && bk % 32 == 0; }
+
+void free_buffers(svg::MapBuffers& b) {
+  void* ptrs[] = {b.kinds, b.classes, b.rowinfo, b.row_ptr, b.entries, b.rowstats, b.stats};
+  for (void* p : ptrs)
+    if (p) (void)hipFree(p);
+  b = svg::MapBuffers{};
+}
+
+template <typename T>
+hipError_t alloc(T** p, size_t count) {
+  return hipMalloc(reinterpret_cast<void**>(p), count * sizeof(T) + 16);
+}
+
+svg_status wait_built(const svg_tile_map* m) {
+  if (m->built) {
+    const hipError_t e = hipEventSynchronize(m->built);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  }
+  return SVG_OK;
+}
+
+svg_status run_build(svg_tile_map* m, hipStream_t stream) {
+  hipError_t e = svg::launch_build_tile_map(m->geom, m->buf, stream);
+  if (e != hipSuccess) return hip_fail(e, "tile-map kernels");
+  e = hipEventRecord(m->built, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* svg_last_error(void) { return g_last_error.c_str(); }
+
+int32_t svg_abi_version(void) { return SVG_ABI_VERSION; }
+
+svg_status svg_build_tile_map(const svg_mask_spec* spec, int32_t tile_q, int32_t tile_k,
+                              void* stream, svg_tile_map** out) {
+  if (!spec) return fail(SVG_ERR_INVALID_ARG, "spec is NULL");
+  if (!out) return fail(SVG_ERR_INVALID_ARG, "out is NULL");
+  if (!spec->head_kind) return fail(SVG_ERR_INVALID_ARG, "spec->head_kind is NULL");
+  if (spec->frames < 1 || spec->grid_h < 1 || spec->grid_w < 1)
+    return fail(SVG_ERR_INVALID_ARG, "frames, grid_h and grid_w must be >= 1");
+  const int64_t S = (int64_t)spec->grid_h * spec->grid_w;
+  const int64_t N = S * spec->frames;
+  if (S > (1 << 30) || N > (1 << 30))
+    return fail(SVG_ERR_INVALID_ARG, "sequence of %lld tokens exceeds 2^30", (long long)N);
+  if (spec->num_heads < 1 || spec->num_heads > 4096)
+    return fail(SVG_ERR_INVALID_ARG, "num_heads %d outside [1, 4096]", spec->num_heads);
+  if (spec->frame_window < 0 || spec->temporal_band < 0)
+    return fail(SVG_ERR_INVALID_ARG, "frame_window and temporal_band must be >= 0");
+  if (spec->round_mode != SVG_ROUND_EXACT && spec->round_mode != SVG_ROUND_TILE)
+    return fail(SVG_ERR_INVALID_ARG, "round_mode %d is not an svg_round_mode", spec->round_mode);
+  for (int32_t h = 0; h < spec->num_heads; ++h) {
+    const int32_t k = spec->head_kind[h];
+    if (k != SVG_HEAD_SPATIAL && k != SVG_HEAD_TEMPORAL && k != SVG_HEAD_DENSE)
+      return fail(SVG_ERR_INVALID_ARG, "head_kind[%d] = %d is not an svg_head_kind", h, k);
+  }
+  if (!tile_q_ok(tile_q))
+    return fail(SVG_ERR_UNSUPPORTED, "tile_q %d: supported are 32, 64, 128 and multiples of 256",
+                tile_q);
+  if (!tile_k_ok(tile_k))
+    return fail(SVG_ERR_UNSUPPORTED, "tile_k %d: supported are multiples of 32 in [32, 1024]",
+                tile_k);
+
+  svg_tile_map* m = new (std::nothrow) svg_tile_map();
+  if (!m) return fail(SVG_ERR_OOM, "host allocation of the map failed");
+  svg::MapGeometry& g = m->geom;
+  g.N = N;
+  g.F = spec->frames;
+  g.S = (int32_t)S;
+  g.H = spec->num_heads;
+  // Windows wider than the sequence behave like the sequence; clamping keeps
+  // every product in range.
+  g.W_f = spec->frame_window < spec->frames ? spec->frame_window : spec->frames;
+  g.W_s = spec->temporal_band < g.S ? spec->temporal_band : g.S;
+  g.sink = spec->sink_first_frame ? 1 : 0;
+  g.round = spec->round_mode;
+  g.BQ = tile_q;
+  g.BK = tile_k;
+  g.nQ = (int32_t)((N + tile_q - 1) / tile_q);
+  g.nK = (int32_t)((N + tile_k - 1) / tile_k);
+  m->kinds.assign(spec->head_kind, spec->head_kind + spec->num_heads);
+
+  hipError_t e = hipGetDevice(&m->device);
+  if (e != hipSuccess) {
+    delete m;
+    return hip_fail(e, "hipGetDevice");
+  }
+  const int64_t R = (int64_t)g.H * g.nQ;
+  svg::MapBuffers& b = m->buf;
+  b.capacity = R * g.nK;
+  if (b.capacity > INT32_MAX) {
+    delete m;
+    return fail(SVG_ERR_UNSUPPORTED, "schedule of %lld entries exceeds int32 indexing",
+                (long long)b.capacity);
+  }
+  if ((e = alloc(&b.kinds, g.H)) != hipSuccess || (e = alloc(&b.classes, R * g.nK)) != hipSuccess ||
+      (e = alloc(&b.rowinfo, R * svg::kRowInfo)) != hipSuccess ||
+      (e = alloc(&b.row_ptr, R + 1)) != hipSuccess ||
+      (e = alloc(&b.entries, b.capacity)) != hipSuccess ||
+      (e = alloc(&b.rowstats, R * svg::kRowStats)) != hipSuccess ||
+      (e = alloc(&b.stats, (int64_t)g.H * svg::kRowStats)) != hipSuccess) {
+    free_buffers(b);
+    delete m;
+    return fail(e == hipErrorOutOfMemory ? SVG_ERR_OOM : SVG_ERR_HIP,
+                "device allocation for the tile map failed: %s", hipGetErrorString(e));
+  }
+  if ((e = hipEventCreateWithFlags(&m->built, hipEventDisableTiming)) != hipSuccess) {
+    free_buffers(b);
+    delete m;
+    return hip_fail(e, "hipEventCreate");
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  e = hipMemcpyAsync(b.kinds, m->kinds.data(), sizeof(int32_t) * g.H, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);  // the host array may go away
+  if (e != hipSuccess) {
+    (void)hipEventDestroy(m->built);
+    free_buffers(b);
+    delete m;
+    return hip_fail(e, "copy of head kinds");
+  }
+  const svg_status s = run_build(m, st);
+  if (s != SVG_OK) {
+    (void)hipStreamSynchronize(st);
+    (void)hipEventDestroy(m->built);
+    free_buffers(b);
+    delete m;
+    return s;
+  }
+  *out = m;
+  return ok();
+}
+
+svg_status svg_tile_map_rebuild(svg_tile_map* map, void* stream) {
+  if (!map) return fail(SVG_ERR_INVALID_ARG, "map is NULL");
+  return run_build(map, reinterpret_cast<hipStream_t>(stream));
+}
+
+svg_status svg_tile_map_info_get(const svg_tile_map* map, svg_tile_map_info* out) {
+  if (!map || !out) return fail(SVG_ERR_INVALID_ARG, "map or out is NULL");
+  const svg::MapGeometry& g = map->geom;
+  out->seq_len = g.N;
+  out->num_heads = g.H;
+  out->tile_q = g.BQ;
+  out->tile_k = g.BK;
+  out->num_q_tiles = g.nQ;
+  out->num_k_tiles = g.nK;
+  out->frames = g.F;
+  out->tokens_per_frame = g.S;
+  out->entry_capacity = map->buf.capacity;
+  return ok();
+}
+
+svg_status svg_tile_map_stats(const svg_tile_map* map, svg_head_stats* per_head,
+                              int32_t num_heads) {
+  if (!map || !per_head) return fail(SVG_ERR_INVALID_ARG, "map or per_head is NULL");
+  if (num_heads != map->geom.H)
+    return fail(SVG_ERR_SHAPE_MISMATCH, "num_heads %d, map has %d", num_heads, map->geom.H);
+  svg_status s = wait_built(map);
+  if (s != SVG_OK) return s;
+  std::vector<int64_t> host((size_t)num_heads * svg::kRowStats);
+  const hipError_t e = hipMemcpy(host.data(), map->buf.stats, host.size() * sizeof(int64_t),
+                                 hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "copy of tile-map stats");
+  for (int32_t h = 0; h < num_heads; ++h) {
+    const int64_t* r = host.data() + (size_t)h * svg::kRowStats;
+    per_head[h] = svg_head_stats{r[0], r[1], r[2], r[3], r[4], r[5], r[6], r[7]};
+  }
+  return ok();
+}
+
+svg_status svg_tile_map_copy_classes(const svg_tile_map* map, uint8_t* host, size_t n) {
+  if (!map || !host) return fail(SVG_ERR_INVALID_ARG, "map or host is NULL");
+  const svg::MapGeometry& g = map->geom;
+  const size_t want = (size_t)g.H * g.nQ * g.nK;
+  if (n != want) return fail(SVG_ERR_SHAPE_MISMATCH, "n = %zu, class map has %zu bytes", n, want);
+  svg_status s = wait_built(map);
+  if (s != SVG_OK) return s;
+  const hipError_t e = hipMemcpy(host, map->buf.classes, want, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "copy of class map");
+  return ok();
+}
+
+svg_status svg_tile_map_copy_schedule(const svg_tile_map* map, int32_t* row_ptr,
+                                      int32_t* n_full, int32_t* sink_ab, int32_t* entries,
+                                      size_t n_entries) {
+  if (!map) return fail(SVG_ERR_INVALID_ARG, "map is NULL");
+  svg_status s = wait_built(map);
+  if (s != SVG_OK) return s;
+  const svg::MapGeometry& g = map->geom;
+  const size_t R = (size_t)g.H * g.nQ;
+  std::vector<int32_t> rp(R + 1);
+  hipError_t e = hipMemcpy(rp.data(), map->buf.row_ptr, (R + 1) * sizeof(int32_t),
+                           hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "copy of row_ptr");
+  if (entries && n_entries < (size_t)rp[R])
+    return fail(SVG_ERR_SHAPE_MISMATCH, "n_entries = %zu, schedule has %d entries", n_entries,
+                rp[R]);
+  if (row_ptr) std::memcpy(row_ptr, rp.data(), (R + 1) * sizeof(int32_t));
+  if (n_full || sink_ab) {
+    std::vector<int32_t> ri(R * svg::kRowInfo);
+    e = hipMemcpy(ri.data(), map->buf.rowinfo, ri.size() * sizeof(int32_t),
+                  hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "copy of row info");
+    for (size_t r = 0; r < R; ++r) {
+      if (n_full) n_full[r] = ri[r * svg::kRowInfo + 0];
+      if (sink_ab) {
+        sink_ab[2 * r] = ri[r * svg::kRowInfo + 2];
+        sink_ab[2 * r + 1] = ri[r * svg::kRowInfo + 3];
+      }
+    }
+  }
+  if (entries && rp[R] > 0) {
+    e = hipMemcpy(entries, map->buf.entries, (size_t)rp[R] * sizeof(int32_t),
+                  hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "copy of schedule entries");
+  }
+  return ok();
+}
+
+svg_status svg_tile_map_destroy(svg_tile_map* map) {
+  if (!map) return ok();
+  svg_status s = wait_built(map);
+  if (map->built) (void)hipEventDestroy(map->built);
+  free_buffers(map->buf);
+  delete map;
+  return s == SVG_OK ? ok() : s;
+}
+
+svg_status svg_attn_fwd(const void* q, const void* k, const void* v, void* o, int64_t seq_len,
+                        int32_t num_heads, int32_t head_dim, float scale,
+                        const int32_t* head_kind, const svg_tile_map* map, uint32_t flags,
+                        void* stream) {
+  if (!q || !k || !v || !o) return fail(SVG_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
+  if (!map) return fail(SVG_ERR_INVALID_ARG, "map is NULL");
+  if (!head_kind) return fail(SVG_ERR_INVALID_ARG, "head_kind is NULL");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(SVG_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (flags & ~(uint32_t)SVG_ATTN_MASK_ALL_TILES)
+    return fail(SVG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  const svg::MapGeometry& g = map->geom;
+  if (seq_len != g.N)
+    return fail(SVG_ERR_SHAPE_MISMATCH, "seq_len %lld, map has %lld", (long long)seq_len,
+                (long long)g.N);
+  if (num_heads != g.H)
+    return fail(SVG_ERR_SHAPE_MISMATCH, "num_heads %d, map has %d", num_heads, g.H);
+  for (int32_t h = 0; h < num_heads; ++h)
+    if (head_kind[h] != map->kinds[h])
+      return fail(SVG_ERR_SHAPE_MISMATCH, "head_kind[%d] = %d, map was built with %d", h,
+                  head_kind[h], map->kinds[h]);
+  if (!svg::attn_supported(head_dim, g.BQ, g.BK))
+    return fail(SVG_ERR_UNSUPPORTED, "head_dim %d with tiles %dx%d has no kernel", head_dim,
+                g.BQ, g.BK);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(SVG_ERR_ALIGNMENT, "q, k, v and o must be 16-byte aligned");
+  const uintptr_t bytes = (uintptr_t)num_heads * (uintptr_t)seq_len * head_dim * 2;
+  const uintptr_t ob = reinterpret_cast<uintptr_t>(o);
+  for (const void* in : {q, k, v}) {
+    const uintptr_t ib = reinterpret_cast<uintptr_t>(in);
+    if (ob < ib + bytes && ib < ob + bytes)
+      return fail(SVG_ERR_INVALID_ARG, "o overlaps an input");
+  }
+  svg::AttnArgs a{q, k, v, o, head_dim, scale, flags};
+  const hipError_t e = svg::launch_attn_fwd(g, map->buf, a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return ok();
+}
+
+svg_status svg_permute_tokens(const void* src, void* dst, int32_t frames,
+                              int32_t tokens_per_frame, int32_t num_heads, int32_t head_dim,
+                              const int32_t* head_kind, int32_t direction, void* stream) {
+  if (!src || !dst || !head_kind) return fail(SVG_ERR_INVALID_ARG, "NULL pointer argument");
+  if (frames < 1 || tokens_per_frame < 1 || num_heads < 1)
+    return fail(SVG_ERR_INVALID_ARG, "frames, tokens_per_frame and num_heads must be >= 1");
+  if ((int64_t)frames * tokens_per_frame > (1 << 30))
+    return fail(SVG_ERR_INVALID_ARG, "sequence exceeds 2^30 tokens");
+  if (head_dim < 8 || head_dim > 1024 || head_dim % 8)
+    return fail(SVG_ERR_UNSUPPORTED, "head_dim %d: multiples of 8 up to 1024", head_dim);
+  if (direction != SVG_TO_KERNEL_LAYOUT && direction != SVG_TO_ORIGINAL_LAYOUT)
+    return fail(SVG_ERR_INVALID_ARG, "direction %d is not an svg_permute_dir", direction);
+  for (int32_t h = 0; h < num_heads; ++h) {
+    const int32_t kd = head_kind[h];
+    if (kd != SVG_HEAD_SPATIAL && kd != SVG_HEAD_TEMPORAL && kd != SVG_HEAD_DENSE)
+      return fail(SVG_ERR_INVALID_ARG, "head_kind[%d] = %d is not an svg_head_kind", h, kd);
+  }
+  if (!aligned16(src) || !aligned16(dst))
+    return fail(SVG_ERR_ALIGNMENT, "src and dst must be 16-byte aligned");
+  const uintptr_t bytes =
+      (uintptr_t)num_heads * (uintptr_t)frames * tokens_per_frame * head_dim * 2;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + bytes && b < a + bytes) return fail(SVG_ERR_INVALID_ARG, "src and dst overlap");
+  const hipError_t e =
+      svg::launch_permute_tokens(src, dst, frames, tokens_per_frame, num_heads, head_dim,
+                                 head_kind, direction, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "permute kernel launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,258 @@
+// Tile-map builder: classify every (BQ x BK) tile of every head as SKIP /
+// FULL / BOUNDARY and compact, per (head, Q tile), the KV tiles to execute.
+//
+// Tile-aware masking: a tile whose existing pairs are all retained runs
+// mask-free, a mixed tile runs the per-element predicate, an empty tile is
+// skipped ("Google Speeds Up Video Diffusion on TPUs with Optimized Sparse
+// Attention", "Efficient Kernel Implementation"; Newsbite "Summary").
+//
+// Counting is exact integer interval arithmetic. Rows of a Q tile are split
+// into runs that share the mask-relevant coordinate (the frame for spatial
+// heads in natural order, the raster index for temporal heads in
+// spatial-major order); every row of a run keeps the same columns, so a
+// tile's count is sum(run length x retained columns of the run in the tile).
+//   spatial run (frame f):  window [max(0,f-Wf)*S, min(F,f+Wf+1)*S) united
+//                           with the sink [0, S)
+//   temporal run (index s): band [max(0,s-Ws)*F, min(S,s+Ws+1)*F) united with
+//                           the sink, the multiples of F
+// Temporal heads execute only the band hull of KV tiles plus the frame-0
+// keys outside it (raster indices [0,a) and [b,S)), so that most tiles are
+// skipped although the strided sink touches every tile.
+#include "svg_internal.hpp"
+
+namespace svg {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ int64_t span(int64_t a, int64_t b) { return b > a ? b - a : 0; }
+__device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// multiples of F in [a, b), a >= 0
+__device__ __forceinline__ int64_t multiples(int64_t a, int64_t b, int64_t F) {
+  return b > a ? cdiv(b, F) - cdiv(a, F) : 0;
+}
+
+struct Counts {
+  int64_t mask;     // retained pairs of the exact mask
+  int64_t contig;   // pairs of the contiguous part (spatial: all; temporal: band)
+};
+
+// Retained columns in [c0, c1) of one row whose run coordinate is v.
+__device__ __forceinline__ Counts row_columns(const MapGeometry& g, int kind,
+                                              int64_t v, int64_t c0, int64_t c1) {
+  Counts r;
+  if (kind == SVG_HEAD_SPATIAL) {
+    const int64_t lo = max<int64_t>(0, v - g.W_f) * g.S;
+    const int64_t hi = min<int64_t>(g.F, v + g.W_f + 1) * g.S;
+    int64_t n = span(max(lo, c0), min(hi, c1));
+    if (g.sink) {
+      n += span(c0, min<int64_t>(g.S, c1));
+      n -= span(max(lo, c0), min(min<int64_t>(hi, g.S), c1));
+    }
+    r.mask = n;
+    r.contig = n;
+  } else {  // temporal
+    const int64_t lo = max<int64_t>(0, v - g.W_s) * g.F;
+    const int64_t hi = min<int64_t>(g.S, v + g.W_s + 1) * g.F;
+    const int64_t a = max(lo, c0), b = min(hi, c1);
+    const int64_t band = span(a, b);
+    r.contig = band;
+    r.mask = band + (g.sink ? multiples(c0, c1, g.F) - multiples(a, max(a, b), g.F) : 0);
+  }
+  return r;
+}
+
+template <int N>
+__device__ void block_sum(int64_t (&v)[N], int64_t* lds) {
+  // lds: kThreads/64 * N int64
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    int64_t x = v[i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_down(x, off, 64);
+    if (lane == 0) lds[wave * N + i] = x;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int64_t s = 0;
+      for (int w = 0; w < kThreads / 64; ++w) s += lds[w * N + i];
+      v[i] = s;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void classify_kernel(MapGeometry g, MapBuffers b) {
+  const int qt = blockIdx.x, h = blockIdx.y;
+  const int64_t row = (int64_t)h * g.nQ + qt;
+  const int kind = b.kinds[h];
+  const int64_t q0 = (int64_t)qt * g.BQ, q1 = min<int64_t>(g.N, q0 + g.BQ);
+  const int64_t rows = q1 - q0;
+
+  int64_t lo = 0, hi = g.nK - 1, sa = 0, sb = g.S;
+  if (kind == SVG_HEAD_TEMPORAL) {
+    const int64_t s0 = q0 / g.F, s1 = (q1 - 1) / g.F;
+    lo = (max<int64_t>(0, s0 - g.W_s) * g.F) / g.BK;
+    hi = ((min<int64_t>(g.S - 1, s1 + g.W_s) + 1) * g.F - 1) / g.BK;
+    if (g.sink) {
+      sa = cdiv(lo * g.BK, g.F);
+      sb = cdiv(min<int64_t>(g.N, (hi + 1) * g.BK), g.F);
+    }
+  }
+  const int64_t unit = (kind == SVG_HEAD_TEMPORAL) ? g.F : g.S;
+
+  // skip, full, boundary, exec_full, exec_boundary, retained
+  int64_t acc[6] = {0, 0, 0, 0, 0, 0};
+  uint8_t* cls_row = b.classes + row * g.nK;
+  for (int64_t kt = threadIdx.x; kt < g.nK; kt += kThreads) {
+    const int64_t c0 = kt * g.BK, c1 = min<int64_t>(g.N, c0 + g.BK);
+    const int64_t area = rows * (c1 - c0);
+    int64_t cnt;
+    if (kind == SVG_HEAD_DENSE) {
+      cnt = area;
+    } else {
+      int64_t mask = 0, contig = 0;
+      for (int64_t v = q0 / unit; v <= (q1 - 1) / unit; ++v) {
+        const int64_t len = min(q1, (v + 1) * unit) - max(q0, v * unit);
+        const Counts c = row_columns(g, kind, v, c0, c1);
+        mask += len * c.mask;
+        contig += len * c.contig;
+      }
+      cnt = mask;
+      if (g.round == SVG_ROUND_TILE) {
+        if (contig > 0)
+          cnt = area;  // the contiguous part is rounded out to the whole tile
+        else if (kind == SVG_HEAD_TEMPORAL)
+          cnt = g.sink ? rows * multiples(c0, c1, g.F) : 0;  // exact strided sink
+        else
+          cnt = 0;
+      }
+    }
+    const uint8_t c = cnt == 0 ? SVG_TILE_SKIP : (cnt == area ? SVG_TILE_FULL : SVG_TILE_BOUNDARY);
+    cls_row[kt] = c;
+    acc[0] += c == SVG_TILE_SKIP;
+    acc[1] += c == SVG_TILE_FULL;
+    acc[2] += c == SVG_TILE_BOUNDARY;
+    const bool run = kt >= lo && kt <= hi;
+    acc[3] += run && c == SVG_TILE_FULL;
+    acc[4] += run && c == SVG_TILE_BOUNDARY;
+    acc[5] += cnt;
+  }
+  __shared__ int64_t lds[kThreads / 64 * 6];
+  block_sum(acc, lds);
+  if (threadIdx.x == 0) {
+    int32_t* ri = b.rowinfo + row * kRowInfo;
+    ri[0] = (int32_t)acc[3];
+    ri[1] = (int32_t)acc[4];
+    ri[2] = (int32_t)sa;
+    ri[3] = (int32_t)sb;
+    ri[4] = (int32_t)lo;
+    ri[5] = (int32_t)hi;
+    ri[6] = 0;
+    ri[7] = 0;
+    int64_t* rs = b.rowstats + row * kRowStats;
+    rs[0] = g.nK;
+    rs[1] = acc[0];
+    rs[2] = acc[1];
+    rs[3] = acc[2];
+    rs[4] = acc[3];
+    rs[5] = acc[4];
+    rs[6] = cdiv(sa, g.BK) + cdiv(g.S - sb, g.BK);
+    rs[7] = acc[5];
+  }
+}
+
+// Exclusive scan of executed tiles per row -> row_ptr (one block).
+__global__ __launch_bounds__(1024) void scan_kernel(int64_t R, const int32_t* rowinfo,
+                                                    int32_t* row_ptr) {
+  __shared__ int64_t part[1024];
+  const int t = threadIdx.x;
+  const int64_t per = (R + 1023) / 1024;
+  const int64_t r0 = t * per, r1 = min(R, r0 + per);
+  int64_t s = 0;
+  for (int64_t r = r0; r < r1; ++r) s += rowinfo[r * kRowInfo] + rowinfo[r * kRowInfo + 1];
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int64_t x = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += x;
+    __syncthreads();
+  }
+  int64_t base = part[t] - s;  // exclusive
+  for (int64_t r = r0; r < r1; ++r) {
+    row_ptr[r] = (int32_t)base;
+    base += rowinfo[r * kRowInfo] + rowinfo[r * kRowInfo + 1];
+  }
+  if (t == 1023) row_ptr[R] = (int32_t)part[1023];
+}
+
+// Ordered compaction of one row: FULL ids of the run range ascending, then
+// BOUNDARY ids ascending.
+__global__ __launch_bounds__(kThreads) void compact_kernel(MapGeometry g, MapBuffers b) {
+  const int qt = blockIdx.x, h = blockIdx.y;
+  const int64_t row = (int64_t)h * g.nQ + qt;
+  const int32_t* ri = b.rowinfo + row * kRowInfo;
+  const int lo = ri[4], hi = ri[5];
+  const uint8_t* cls_row = b.classes + row * g.nK;
+  int32_t* out = b.entries + b.row_ptr[row];
+  __shared__ int wave_tot[kThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int pos = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const uint8_t want = pass == 0 ? SVG_TILE_FULL : SVG_TILE_BOUNDARY;
+    for (int c = lo; c <= hi; c += kThreads) {
+      const int kt = c + threadIdx.x;
+      const bool flag = kt <= hi && cls_row[kt] == want;
+      const uint64_t m = __ballot(flag);
+      const int before = __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == 0) wave_tot[wave] = __popcll(m);
+      __syncthreads();
+      int off = 0, tot = 0;
+      for (int w = 0; w < kThreads / 64; ++w) {
+        off += w < wave ? wave_tot[w] : 0;
+        tot += wave_tot[w];
+      }
+      if (flag) out[pos + off + before] = kt;
+      pos += tot;
+      __syncthreads();
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void stats_kernel(MapGeometry g, MapBuffers b) {
+  const int h = blockIdx.x;
+  int64_t acc[kRowStats] = {};
+  for (int64_t qt = threadIdx.x; qt < g.nQ; qt += kThreads) {
+    const int64_t* rs = b.rowstats + ((int64_t)h * g.nQ + qt) * kRowStats;
+#pragma unroll
+    for (int i = 0; i < kRowStats; ++i) acc[i] += rs[i];
+  }
+  __shared__ int64_t lds[kThreads / 64 * kRowStats];
+  block_sum(acc, lds);
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < kRowStats; ++i) b.stats[h * kRowStats + i] = acc[i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_build_tile_map(const MapGeometry& g, const MapBuffers& b,
+                                 hipStream_t stream) {
+  const dim3 rows_grid(g.nQ, g.H);
+  hipLaunchKernelGGL(classify_kernel, rows_grid, dim3(kThreads), 0, stream, g, b);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream,
+                     (int64_t)g.H * g.nQ, (const int32_t*)b.rowinfo, b.row_ptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_kernel, rows_grid, dim3(kThreads), 0, stream, g, b);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(stats_kernel, dim3(g.H), dim3(kThreads), 0, stream, g, b);
+  return hipGetLastError();
+}
+
+}  // namespace svg

@@ -1,0 +1,144 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+bad arguments before any HIP call (no GPU needed)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import structured_sparse_attention_amd as svg
+from structured_sparse_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svg_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(svg_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return svg.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in svg_attn.h but not exported"
+    assert sorted(svg.EXPORTED) == names
+
+
+def test_abi_version(lib):
+    assert svg.abi_version() == 1
+
+
+def _spec(kinds, frames=4, gh=8, gw=8, wf=1, ws=8, sink=1, rnd=0):
+    arr = np.asarray(kinds, dtype=np.int32)
+    s = _lib.MaskSpec(frames, gh, gw, len(arr), arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                      wf, ws, sink, rnd)
+    return s, arr
+
+
+def _build(lib, spec, bq=32, bk=32):
+    out = ctypes.c_void_p()
+    st = lib.svg_build_tile_map(ctypes.byref(spec) if spec is not None else None, bq, bk,
+                                None, ctypes.byref(out))
+    return st, out
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (dict(frames=0), svg.ERR_INVALID_ARG),
+    (dict(gh=0), svg.ERR_INVALID_ARG),
+    (dict(wf=-1), svg.ERR_INVALID_ARG),
+    (dict(ws=-3), svg.ERR_INVALID_ARG),
+    (dict(rnd=7), svg.ERR_INVALID_ARG),
+    (dict(kinds=[0, 5]), svg.ERR_INVALID_ARG),
+    (dict(kinds=[]), svg.ERR_INVALID_ARG),
+    (dict(frames=1 << 16, gh=1 << 8, gw=1 << 8), svg.ERR_INVALID_ARG),
+])
+def test_build_rejects_bad_spec(lib, mutate, status):
+    args = dict(kinds=[0, 1])
+    args.update(mutate)
+    spec, keep = _spec(**args)
+    st, out = _build(lib, spec)
+    assert st == status
+    assert not out.value
+    assert lib.svg_last_error().decode()
+
+
+@pytest.mark.parametrize("bq,bk", [(48, 32), (96, 64), (300, 128), (256, 48), (256, 16),
+                                   (256, 2048), (0, 128), (-256, 128)])
+def test_build_rejects_unsupported_tiles(lib, bq, bk):
+    spec, keep = _spec([0, 1])
+    st, out = _build(lib, spec, bq, bk)
+    assert st == svg.ERR_UNSUPPORTED
+    assert not out.value
+
+
+def test_build_null_arguments(lib):
+    assert _build(lib, None)[0] == svg.ERR_INVALID_ARG
+    spec, keep = _spec([0, 1])
+    assert lib.svg_build_tile_map(ctypes.byref(spec), 32, 32, None, None) == svg.ERR_INVALID_ARG
+    spec.head_kind = None
+    assert _build(lib, spec)[0] == svg.ERR_INVALID_ARG
+
+
+def test_map_calls_reject_null(lib):
+    assert lib.svg_tile_map_destroy(None) == svg.OK
+    info = _lib.TileMapInfo()
+    assert lib.svg_tile_map_info_get(None, ctypes.byref(info)) == svg.ERR_INVALID_ARG
+    assert lib.svg_tile_map_rebuild(None, None) == svg.ERR_INVALID_ARG
+    assert lib.svg_tile_map_stats(None, None, 1) == svg.ERR_INVALID_ARG
+    assert lib.svg_tile_map_copy_classes(None, None, 0) == svg.ERR_INVALID_ARG
+    assert lib.svg_tile_map_copy_schedule(None, None, None, None, None, 0) == svg.ERR_INVALID_ARG
+
+
+def test_attn_rejects_bad_arguments_before_hip(lib):
+    kinds = np.array([0, 1], dtype=np.int32)
+    kp = kinds.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    p = 1 << 20  # never dereferenced: validation fails first
+    f = lib.svg_attn_fwd
+    assert f(None, p, p, p, 256, 2, 64, 0.125, kp, p, 0, None) == svg.ERR_INVALID_ARG
+    assert f(p, p, p, p, 256, 2, 64, 0.125, kp, None, 0, None) == svg.ERR_INVALID_ARG
+    assert f(p, p, p, p, 256, 2, 64, 0.125, None, p, 0, None) == svg.ERR_INVALID_ARG
+    assert f(p, p, p, p, 256, 2, 64, -1.0, kp, p, 0, None) == svg.ERR_INVALID_ARG
+    assert f(p, p, p, p, 256, 2, 64, float("inf"), kp, p, 0, None) == svg.ERR_INVALID_ARG
+    assert f(p, p, p, p, 256, 2, 64, 0.125, kp, p, 8, None) == svg.ERR_INVALID_ARG
+    assert "flags" in lib.svg_last_error().decode()
+
+
+def test_permute_rejects_bad_arguments_before_hip(lib):
+    kinds = np.array([0, 1], dtype=np.int32)
+    kp = kinds.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    f = lib.svg_permute_tokens
+    a, b = 1 << 20, 1 << 30
+    assert f(None, b, 4, 64, 2, 64, kp, 0, None) == svg.ERR_INVALID_ARG
+    assert f(a, b, 0, 64, 2, 64, kp, 0, None) == svg.ERR_INVALID_ARG
+    assert f(a, b, 4, 64, 2, 60, kp, 0, None) == svg.ERR_UNSUPPORTED
+    assert f(a, b, 4, 64, 2, 64, kp, 2, None) == svg.ERR_INVALID_ARG
+    assert f(a + 8, b, 4, 64, 2, 64, kp, 0, None) == svg.ERR_ALIGNMENT
+    assert f(a, a + 16, 4, 64, 2, 64, kp, 0, None) == svg.ERR_INVALID_ARG  # overlap
+    bad = np.array([0, 3], dtype=np.int32)
+    assert f(a, b, 4, 64, 2, 64, bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 0,
+             None) == svg.ERR_INVALID_ARG
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        _load_fresh(str(tmp_path / "nope.so"))
+
+
+def _load_fresh(path):
+    saved = _lib._lib
+    _lib._lib = None
+    try:
+        return _lib.load(path)
+    finally:
+        _lib._lib = saved

@@ -1,0 +1,223 @@
+"""HIP attention forward vs the CPU oracle, element by element.
+
+Gate (from the target): max |O_gpu - O_ref| <= 2e-2 and mean |.| <= 2e-3 with
+bf16 inputs. Because |O| is about 1e-2 at long sequences, that gate alone
+would miss partial mask errors, so every case also checks relative L2 error
+<= 1e-2 (a correct kernel sits near 3e-3: bf16 rounding of P and of O), and
+two probes make mask errors large:
+  * Q = 0 makes every retained key weigh exactly 1/n_row; V columns that are
+    indicators of key regions then give O = (kept keys in region)/n_row,
+    exact up to bf16 output rounding, so a dropped or doubled tile moves a
+    value by several percent;
+  * V = 1 gives O = 1 up to rounding of P.
+"""
+from __future__ import annotations
+
+from functools import lru_cache
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+import structured_sparse_attention_amd as svg
+from gpu_harness import (build_map, from_device, run_attention, say, to_device,
+                         to_kernel_layout, to_original_layout)
+from oracle_cases import masks_of, params_of, widen
+from oracle_pool import oracle_rows
+from test_oracle_pins import RAGGED, RAGGED_NOSINK
+
+pytestmark = pytest.mark.gpu
+
+TOL_MAX, TOL_MEAN, TOL_REL_L2 = 2e-2, 2e-3, 1e-2
+
+
+def _aligned(w):
+    return si.Workload(w.name + "-ta", w.frames, w.grid_h, w.grid_w, w.head_kinds, w.head_dim,
+                       w.frame_window, w.band, w.sink, w.tile_q, w.tile_k, True, w.seed)
+
+
+def check(o_gpu, o_ref, what):
+    err = np.abs(o_gpu.astype(np.float64) - o_ref)
+    mx, mean = float(err.max()), float(err.mean())
+    rel = float(np.linalg.norm(o_gpu - o_ref) / max(np.linalg.norm(o_ref), 1e-30))
+    say(f"  {what}: max_abs={mx:.3e} mean_abs={mean:.3e} rel_l2={rel:.3e}")
+    assert np.all(np.isfinite(o_gpu)), what
+    assert mx <= TOL_MAX and mean <= TOL_MEAN, (what, mx, mean)
+    assert rel <= TOL_REL_L2, (what, rel)
+
+
+@lru_cache(maxsize=4)
+def inputs(w: si.Workload):
+    return si.draw_qkv(w, return_rng=True)
+
+
+SMALL = [si.workload("tiny"), si.workload("tiny-misaligned"), RAGGED, RAGGED_NOSINK,
+         _aligned(si.workload("tiny")), _aligned(si.workload("tiny-misaligned")),
+         _aligned(RAGGED),
+         RAGGED.with_tiles(128, 64), RAGGED.with_tiles(512, 256), RAGGED.with_tiles(32, 96),
+         si.Workload("one-frame", 1, 7, 9, ("spatial", "temporal", "dense"), 64, 0, 3, True,
+                     32, 32, False, seed=31),
+         si.Workload("one-token", 1, 1, 1, ("spatial", "temporal"), 64, 0, 0, True, 32, 32,
+                     False, seed=32),
+         si.Workload("wide", 3, 5, 7, ("spatial", "temporal"), 64, 9, 999, True, 64, 96,
+                     False, seed=33),
+         si.Workload("narrow", 6, 4, 5, ("spatial", "temporal"), 64, 0, 0, False, 32, 64,
+                     False, seed=34),
+         si.Workload("d128-ragged", 5, 9, 10, ("spatial", "temporal", "dense", "temporal"), 128,
+                     1, 13, True, 256, 128, False, seed=35),
+         si.Workload("d128-multi-tile", 6, 12, 16, ("spatial", "temporal"), 128, 1, 40, True,
+                     256, 128, False, seed=36)]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: f"{w.name}@{w.tile_q}x{w.tile_k}")
+def test_full_output_parity_small(w):
+    say(f"[attn] {w.name} N={w.seq_len} H={w.num_heads} d={w.head_dim} "
+        f"BQ={w.tile_q} BK={w.tile_k} aligned={w.tile_aligned}")
+    Q, K, V, _ = inputs(w)
+    ref = oracle.attention(widen(Q), widen(K), widen(V), masks_of(w))
+    for flags in (0, svg.ATTN_MASK_ALL_TILES):
+        o = run_attention(w, Q, K, V, flags=flags)
+        check(o, ref, f"flags={flags}")
+
+
+def _sample_rows(w, n, seed=123):
+    rng = np.random.default_rng(seed)
+    N = w.seq_len
+    # first / last tokens, frame edges, plus random tokens
+    fixed = [0, 1, N - 1, N - 2, w.tokens_per_frame - 1, w.tokens_per_frame, N // 2]
+    rows = np.unique(np.concatenate([fixed, rng.choice(N, n - len(fixed), replace=False)]))
+    return rows.astype(np.int64)
+
+
+@pytest.mark.parametrize("name", ["main", "dense", "tile-aligned"])
+def test_full_size_sampled_rows(name):
+    w = si.workload(name)
+    say(f"[attn-full] {w.name} N={w.seq_len} sampled rows")
+    Q, K, V, _ = inputs(w)
+    o = run_attention(w, Q, K, V)
+    rows = _sample_rows(w, 192)
+    ref = oracle_rows(w, Q, K, V, masks_of(w), rows)
+    check(o[:, rows], ref, name)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("bq,bk", si.SWEEP_TILES)
+def test_tile_aligned_sweep_sampled_rows(bq, bk):
+    w = si.workload("tile-aligned").with_tiles(bq, bk)
+    say(f"[attn-sweep] {w.name}")
+    Q, K, V, _ = inputs(si.workload("tile-aligned"))
+    o = run_attention(w, Q, K, V)
+    rows = _sample_rows(w, 64, seed=bq * 1000 + bk)
+    ref = oracle_rows(w, Q, K, V, masks_of(w), rows)
+    check(o[:, rows], ref, w.name)
+
+
+@pytest.mark.timeout(1200)
+def test_1440p_query_subset():
+    w = si.workload("1440p")
+    say(f"[attn-1440p] N={w.seq_len}: drawing inputs")
+    Q, K, V, rng = si.draw_qkv(w, return_rng=True)
+    rows = si.draw_query_subset(w, w.query_subset, rng)
+    say("[attn-1440p] GPU run")
+    o = run_attention(w, Q, K, V)
+    o_rows = o[:, rows]
+    del o
+    say(f"[attn-1440p] oracle on {len(rows)} queries x {w.num_heads} heads")
+    ref = oracle_rows(w, Q, K, V, masks_of(w), rows)
+    check(o_rows, ref, "1440p subset")
+
+
+def _probe_values(w):
+    """V columns: indicators of key regions (frames, raster buckets, frame 0)."""
+    N, S, F, d = w.seq_len, w.tokens_per_frame, w.frames, w.head_dim
+    t = np.arange(N)
+    f, s = t // S, t % S
+    cols = [np.ones(N), (f == 0).astype(float)]
+    cols += [(f == x).astype(float) for x in range(F)]
+    nb = max(1, min(d - len(cols), 32))
+    edges = np.linspace(0, S, nb + 1).astype(int)
+    cols += [((s >= edges[i]) & (s < edges[i + 1])).astype(float) for i in range(nb)]
+    V = np.zeros((N, d))
+    for i, c in enumerate(cols[:d]):
+        V[:, i] = c
+    return V
+
+
+@pytest.mark.parametrize("name", ["tiny-misaligned", "main"])
+def test_zero_query_count_probe(name):
+    w = si.workload(name)
+    say(f"[probe-q0] {w.name}")
+    H, N, d = w.num_heads, w.seq_len, w.head_dim
+    _, K, _, _ = inputs(w)
+    v1 = _probe_values(w)
+    Vb = np.broadcast_to(si.f32_to_bf16_bits(v1.astype(np.float32)), (H, N, d)).copy()
+    Qb = np.zeros((H, N, d), dtype=np.uint16)
+    for flags in (0, svg.ATTN_MASK_ALL_TILES):
+        o = run_attention(w, Qb, K, Vb, flags=flags)
+        rows = np.arange(N) if N <= 4096 else _sample_rows(w, 96)
+        ref = oracle_rows(w, Qb, K, Vb, masks_of(w), rows)
+        got = o[:, rows].astype(np.float64)
+        # bf16 output rounding: half an ulp, 2^-9 relative
+        bad = np.abs(got - ref) > (2.0 ** -8) * np.abs(ref) + 1e-7
+        say(f"  flags={flags}: {int(bad.sum())} of {bad.size} outside bf16 rounding")
+        assert not bad.any()
+
+
+@pytest.mark.parametrize("name", ["tiny", "main"])
+def test_v_ones_probe(name):
+    w = si.workload(name)
+    say(f"[probe-v1] {w.name}")
+    Q, K, _, _ = inputs(w)
+    ones = np.full(Q.shape, 0x3F80, dtype=np.uint16)  # bf16 1.0
+    o = run_attention(w, Q, K, ones)
+    dev = np.abs(o - 1.0).max()
+    say(f"  max |O - 1| = {dev:.3e}")
+    assert dev <= 2.0 ** -7
+
+
+@pytest.mark.parametrize("name", ["tiny-misaligned", "main"])
+def test_permutation_matches_oracle_layout(name):
+    w = si.workload(name)
+    say(f"[permute] {w.name}")
+    Q, _, _, _ = inputs(w)
+    x = to_device(Q)
+    y = to_kernel_layout(w, x)
+    z = to_original_layout(w, y)
+    import torch
+    torch.cuda.synchronize()
+    yb = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    zb = z.view(torch.int16).cpu().numpy().view(np.uint16)
+    p = params_of(w)
+    for h, kind in enumerate(w.head_kinds):
+        np.testing.assert_array_equal(yb[h], oracle.to_kernel_layout(p, kind, Q[h]))
+    np.testing.assert_array_equal(zb, Q)
+
+
+def test_shape_and_kind_mismatch_rejected():
+    w = si.workload("tiny")
+    Q, K, V, _ = inputs(w)
+    q, k, v = (to_device(x) for x in (Q, K, V))
+    o = q.new_empty(q.shape)
+    tm = build_map(w)
+    with pytest.raises(svg.SvgError) as e:
+        svg.svg_attn_fwd(q, k, v, o, ["temporal", "temporal"], tm)
+    assert e.value.status == svg.ERR_SHAPE_MISMATCH
+    with pytest.raises(svg.SvgError) as e:
+        svg.svg_attn_fwd(q[:1].contiguous(), k[:1].contiguous(), v[:1].contiguous(),
+                         o[:1].contiguous(), ["spatial"], tm)
+    assert e.value.status == svg.ERR_SHAPE_MISMATCH
+    with pytest.raises(svg.SvgError) as e:
+        svg.svg_attn_fwd(q, k, v, q, w.head_kinds, tm)   # output aliases input
+    assert e.value.status == svg.ERR_INVALID_ARG
+    tm.destroy()
+
+
+def test_repeated_calls_are_deterministic():
+    w = si.workload("tiny-misaligned")
+    Q, K, V, _ = inputs(w)
+    tm = build_map(w)
+    a = run_attention(w, Q, K, V, tile_map=tm)
+    b = run_attention(w, Q, K, V, tile_map=tm)
+    np.testing.assert_array_equal(a, b)
+    tm.destroy()
