@@ -47,6 +47,7 @@ struct KParams {
   float c;       // scale * log2(e)
   float thr;     // lazy-rescale threshold in raw score units
   int32_t mask_all;
+  int32_t round_tile;  // the map rounds the contiguous mask part to whole tiles
 };
 
 struct Step {
@@ -177,8 +178,32 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
       win_hi[qb] = p.N;
     }
   }
-  const int sink_lim = (kind == SVG_HEAD_SPATIAL && p.sink) ? p.S : 0;
+  int sink_lim = (kind == SVG_HEAD_SPATIAL && p.sink) ? p.S : 0;
   const bool sink_mod = kind == SVG_HEAD_TEMPORAL && p.sink;
+  if (p.round_tile && kind != SVG_HEAD_DENSE) {
+    // Tile-aligned mask: a pair is kept when its (BQ x BK) tile holds any pair
+    // of the contiguous mask part, so the bound is the same for every row of
+    // the map's Q tile: the union of its rows' windows (or bands), widened to
+    // whole KV tiles; the spatial sink [0, S) is widened the same way and the
+    // temporal strided sink stays exact.
+    const int t0 = qt * p.BQ, t1 = min(p.N, t0 + p.BQ) - 1;
+    int lo, hi;
+    if (kind == SVG_HEAD_SPATIAL) {
+      lo = max(0, t0 / p.S - p.W_f) * p.S;
+      hi = min(p.F, t1 / p.S + p.W_f + 1) * p.S;
+    } else {
+      lo = max(0, t0 / p.F - p.W_s) * p.F;
+      hi = min(p.S, t1 / p.F + p.W_s + 1) * p.F;
+    }
+    lo = lo / p.BK * p.BK;
+    hi = min(p.N, (hi + p.BK - 1) / p.BK * p.BK);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      win_lo[qb] = lo;
+      win_hi[qb] = hi;
+    }
+    if (sink_lim > 0) sink_lim = min(p.N, (sink_lim + p.BK - 1) / p.BK * p.BK);
+  }
 
   f32x16 o[D / 32][QB];
 #pragma unroll
@@ -449,6 +474,7 @@ hipError_t launch_attn_fwd(const MapGeometry& g, const MapBuffers& b, const Attn
   kp.c = a.scale * 1.4426950408889634f;
   kp.thr = 8.0f / kp.c;
   kp.mask_all = (a.flags & SVG_ATTN_MASK_ALL_TILES) ? 1 : 0;
+  kp.round_tile = g.round == SVG_ROUND_TILE ? 1 : 0;
   if (kp.total_wg <= 0) return hipSuccess;
   return a.head_dim == 128 ? launch_d<128>(c, kp, stream) : launch_d<64>(c, kp, stream);
 }
