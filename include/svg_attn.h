@@ -188,11 +188,12 @@ svg_status svg_tile_map_destroy(svg_tile_map* map);
  *               aligned, in each head's kernel layout; o must not overlap
  *               q, k or v. The caller owns all four.
  *   head_dim:   64 or 128. scale > 0 and finite (normally 1/sqrt(head_dim)).
+ *               One head (seq_len * head_dim * 2 bytes) must be under 2 GiB.
  *   head_kind:  host [num_heads]; must equal the kinds the map was built with.
  *   map:        built for the same seq_len and num_heads.
  *   flags:      0 or SVG_ATTN_MASK_ALL_TILES.
  * Rows with no retained key would give 0 (the masks here always keep one).
- * Errors: INVALID_ARG, UNSUPPORTED (head_dim), SHAPE_MISMATCH (seq_len,
+ * Errors: INVALID_ARG, UNSUPPORTED (head_dim, head size), SHAPE_MISMATCH (seq_len,
  * num_heads, head kinds vs the map), ALIGNMENT, HIP (launch failure). */
 svg_status svg_attn_fwd(const void* q, const void* k, const void* v, void* o,
                         int64_t seq_len, int32_t num_heads, int32_t head_dim,

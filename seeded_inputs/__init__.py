@@ -14,15 +14,20 @@ temporal heads ("Google Speeds Up Video Diffusion on TPUs with Optimized Sparse
 Attention", section "Sparse Attention Patterns"). No dataset is involved.
 
 Draw recipe (fixed here because the pages give none):
-  * ``numpy.random.default_rng(seed)``;
-  * ``standard_normal((H, N, d), float32)`` for Q, then K, then V, in the
-    original frame-major token order t = f*S + s;
+  * one independent stream per tensor and head:
+    ``numpy.random.default_rng([seed, tensor, head])`` with tensor 0, 1, 2
+    for Q, K, V, drawing ``standard_normal((N, d), float32)`` in the original
+    frame-major token order t = f*S + s (the streams are filled in parallel
+    threads, which keeps the 302,400-token workload quick to generate);
   * each value rounded to bf16 with round-to-nearest-even;
-  * an optional query subset is drawn afterwards from the same generator.
+  * an optional query subset comes from its own stream,
+    ``default_rng([seed, 3])``: distinct tokens, sorted.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field, replace
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, replace
 from typing import Dict, List, Optional, Tuple
 
 import numpy as np
@@ -128,35 +133,32 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _rng(seed: int) -> np.random.Generator:
-    return np.random.default_rng(seed)
+def _draw_head(seed: int, tensor: int, head: int, n: int, d: int) -> np.ndarray:
+    x = np.empty((n, d), dtype=np.float32)
+    np.random.default_rng([seed, tensor, head]).standard_normal(out=x, dtype=np.float32)
+    return f32_to_bf16_bits(x)
 
 
-def draw_qkv(w: Workload, seed: Optional[int] = None,
-             return_rng: bool = False):
+def draw_qkv(w: Workload, seed: Optional[int] = None):
     """Draw Q, K, V as bf16 bit patterns, shape (H, N, d), original order."""
-    rng = _rng(w.seed if seed is None else seed)
-    shape = (w.num_heads, w.seq_len, w.head_dim)
-    out = []
-    for _ in range(3):
-        out.append(f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32)))
-    if return_rng:
-        return out[0], out[1], out[2], rng
+    seed = w.seed if seed is None else seed
+    H, N, d = w.num_heads, w.seq_len, w.head_dim
+    out = [np.empty((H, N, d), dtype=np.uint16) for _ in range(3)]
+
+    def fill(job):
+        t, h = job
+        out[t][h] = _draw_head(seed, t, h, N, d)
+
+    jobs = [(t, h) for t in range(3) for h in range(H)]
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), len(jobs)))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(fill, jobs))
     return out[0], out[1], out[2]
 
 
-def draw_query_subset(w: Workload, count: int,
-                      rng: Optional[np.random.Generator] = None) -> np.ndarray:
-    """Sorted distinct original-order query tokens, drawn after Q, K, V.
-
-    Pass the generator returned by ``draw_qkv(..., return_rng=True)`` to get
-    the subset that follows the inputs; without one, the generator is
-    re-seeded and advanced past the three input draws.
-    """
-    if rng is None:
-        rng = _rng(w.seed)
-        shape = (w.num_heads, w.seq_len, w.head_dim)
-        for _ in range(3):
-            rng.standard_normal(shape, dtype=np.float32)
+def draw_query_subset(w: Workload, count: int, seed: Optional[int] = None) -> np.ndarray:
+    """Sorted distinct original-order query tokens from their own stream."""
+    seed = w.seed if seed is None else seed
+    rng = np.random.default_rng([seed, 3])
     idx = rng.choice(w.seq_len, size=min(count, w.seq_len), replace=False)
     return np.sort(idx).astype(np.int64)

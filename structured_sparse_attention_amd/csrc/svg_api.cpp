@@ -295,6 +295,9 @@ svg_status svg_attn_fwd(const void* q, const void* k, const void* v, void* o, in
     if (head_kind[h] != map->kinds[h])
       return fail(SVG_ERR_SHAPE_MISMATCH, "head_kind[%d] = %d, map was built with %d", h,
                   head_kind[h], map->kinds[h]);
+  if (seq_len * head_dim * 2 >= ((int64_t)1 << 31))
+    return fail(SVG_ERR_UNSUPPORTED, "one head of %lld x %d bf16 values exceeds 2 GiB",
+                (long long)seq_len, head_dim);
   if (!svg::attn_supported(head_dim, g.BQ, g.BK))
     return fail(SVG_ERR_UNSUPPORTED, "head_dim %d with tiles %dx%d has no kernel", head_dim,
                 g.BQ, g.BK);
