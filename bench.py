@@ -9,17 +9,22 @@ their kernel layout once, outside the timed region (the pages' kernel timings
 exclude token permutation).
 
 Prints one JSON line. `value` is effective TFLOP/s over retained pairs
-(4 * d * retained pairs per step / step time). The dense baseline (all-true
-mask through the same kernel) is timed too and reported as `dense_ms`.
+(4 * d * retained pairs per step / step time). Alongside, under "extra": the
+attention kernel alone (HIP events around each launch on the launch stream),
+the tile-map build, the same-shape dense run through the same kernel, the
+naive traversal (mask evaluated on every executed tile) and the tile-aligned
+variant; "cpu_baseline" times the float64 oracle on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
-                    [--workload main] [--profile] [--copy-calibration]
+                    [--no-extras] [--cpu-rows 12288] [--profile] [--copy-calibration]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -28,8 +33,11 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
-PEAK_HBM_GBS = 8000.0
+# MI355X dense bf16 MFMA peak: 256 CU x 2.4 GHz x 4096 FLOP/clk (the published 2.5 PFLOP/s)
+PEAK_BF16_TFLOPS = 2516.6
+KERNEL_SRC = os.path.join(ROOT, "structured_sparse_attention_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_fwd_main_hbm_traffic.md")
+METRIC = "sparse attn fwd ms + effective TFLOP/s (retained pairs) at 75,600 tok×10 heads×d128"
 
 
 def log(msg):
@@ -43,10 +51,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="main")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=96, help="oracle query rows per head")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the dense, naive and tile-aligned runs")
+    ap.add_argument("--cpu-rows", type=int, default=12288, help="oracle query rows per head")
     ap.add_argument("--profile", action="store_true",
-                    help="few steps, no CPU baseline, no dense run (for rocprofv3)")
+                    help="few steps, main workload only (for rocprofv3)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -81,8 +90,11 @@ def device_inputs(w):
     return out, (Q, K, V)
 
 
-def time_steps(w, q, k, v, o, steps, warmup):
-    """Returns (ms per step, mean attention-kernel ms, mean map ms, stats)."""
+def time_steps(w, q, k, v, o, steps, warmup, flags=0):
+    """Time `steps` steps (map rebuild + attention) on the current stream.
+
+    Returns (ms per step, attention-kernel ms list, map ms list, per-head stats).
+    """
     import torch
     import structured_sparse_attention_amd as svg
     tm = svg.svg_build_tile_map(
@@ -92,8 +104,7 @@ def time_steps(w, q, k, v, o, steps, warmup):
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         tm.rebuild(stream)
-        svg.svg_attn_fwd(q, k, v, o, w.head_kinds, tm, stream=stream)
-    torch.cuda.synchronize()
+        svg.svg_attn_fwd(q, k, v, o, w.head_kinds, tm, flags=flags, stream=stream)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -103,97 +114,156 @@ def time_steps(w, q, k, v, o, steps, warmup):
         ev[i][0].record(stream)
         tm.rebuild(stream)
         ev[i][1].record(stream)
-        svg.svg_attn_fwd(q, k, v, o, w.head_kinds, tm, stream=stream)
+        svg.svg_attn_fwd(q, k, v, o, w.head_kinds, tm, flags=flags, stream=stream)
         ev[i][2].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     total = t0.elapsed_time(t1)
-    attn = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    amap = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    attn = [e[1].elapsed_time(e[2]) for e in ev]
+    amap = [e[0].elapsed_time(e[1]) for e in ev]
     tm.destroy()
     return total / steps, attn, amap, stats
 
 
+# ------------------------------------------------------------------ CPU oracle
+
+_POOL = {}
+
+
+def _oracle_task(args):
+    import oracle
+    import seeded_inputs as si
+    h, rows = args
+    w, Q, K, V, masks = (_POOL[k] for k in ("w", "Q", "K", "V", "masks"))
+    widen = lambda b: si.bf16_bits_to_f32(b).astype(np.float64)
+    oracle.attention_rows(widen(Q[h]), widen(K[h]), widen(V[h]), masks[h], rows)
+    return len(rows)
+
+
 def cpu_baseline(w, Q, K, V, rows_per_head):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+    """The oracle, as it stands, on a bounded sample of the same workload.
+
+    Row blocks of 128 queries run in a process pool, one process per host core
+    (capped at 16), each with single-threaded BLAS.
+    """
+    from multiprocessing import get_context
     import oracle
     params = oracle.MaskParams(w.frames, w.grid_h, w.grid_w, w.frame_window, w.band, w.sink)
     masks = [oracle.HeadMask(params, kd, w.tile_aligned, w.tile_q, w.tile_k)
              for kd in w.head_kinds]
     rng = np.random.default_rng(7)
     rows = np.sort(rng.choice(w.seq_len, rows_per_head, replace=False))
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1)
     except Exception:
-        threads = 1
-    import seeded_inputs as si
-    pairs = 0
+        limit = None
+    _POOL.update(w=w, Q=Q, K=K, V=V, masks=masks)
+    tasks = [(h, rows[i:i + 128]) for h in range(w.num_heads) for i in range(0, len(rows), 128)]
+    pairs = sum(int(masks[h].original_block(rows, np.arange(w.seq_len)).sum())
+                for h in range(w.num_heads))
     t = time.perf_counter()
-    for h in range(w.num_heads):
-        k = si.bf16_bits_to_f32(K[h]).astype(np.float64)
-        v = si.bf16_bits_to_f32(V[h]).astype(np.float64)
-        q = si.bf16_bits_to_f32(Q[h]).astype(np.float64)
-        oracle.attention_rows(q, k, v, masks[h], rows)
-        pairs += int(masks[h].original_block(rows, np.arange(w.seq_len)).sum())
+    with get_context("fork").Pool(cores) as pool:
+        done = sum(pool.map(_oracle_task, tasks))
     dt = time.perf_counter() - t
+    assert done == rows_per_head * w.num_heads
+    if limit is not None:
+        limit.restore_original_limits()
     tflops = 4.0 * w.head_dim * pairs / dt / 1e12
-    return {"value": tflops, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": tflops, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": round(dt, 2),
             "sample": f"{rows_per_head} query rows x {w.num_heads} heads of the {w.name} "
-                      f"workload against all {w.seq_len} keys (float64 explicit-mask "
-                      f"attention, {pairs} retained pairs)"}
+                      f"workload against all {w.seq_len} keys: float64 explicit-mask attention, "
+                      f"{pairs} retained pairs, {cores} processes with single-threaded BLAS"}
+
+
+# ------------------------------------------------------------------ roofline
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    text = open(TRAFFIC_PROFILE).read()
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
+    if not m or not b:
+        return None
+    cur = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    return int(b.group(1)) if m.group(1) == cur else None
 
 
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); the path has no "
-              f"multi-GPU mode", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): the path is measured "
+              f"on one GPU's share at its real shape and has no multi-GPU mode",
+              file=sys.stderr)
         sys.exit(2)
     if a.copy_calibration:
         return copy_calibration()
     import torch
     import seeded_inputs as si
     if a.profile:
-        a.steps, a.warmup, a.no_cpu_baseline, a.no_dense = min(a.steps, 5), 1, True, True
+        a.steps, a.warmup, a.no_cpu_baseline, a.no_extras = min(a.steps, 5), 1, True, True
     w = si.workload(a.workload)
     log(f"[bench] workload {w.name}: N={w.seq_len} H={w.num_heads} d={w.head_dim} "
         f"tiles {w.tile_q}x{w.tile_k}")
     (q, k, v), host = device_inputs(w)
     o = torch.empty_like(q)
-    ms, attn_ms, map_ms, stats = time_steps(w, q, k, v, o, a.steps, a.warmup)
+    ms, attn, amap, stats = time_steps(w, q, k, v, o, a.steps, a.warmup)
     pairs = sum(s["retained_pairs"] for s in stats)
     flop = 4.0 * w.head_dim * pairs
     value = flop / (ms * 1e-3) / 1e12
+    attn_ms = float(np.mean(attn))
     achieved = flop / (attn_ms * 1e-3) / 1e12
-    log(f"[bench] step {ms:.3f} ms (attention {attn_ms:.3f} ms, map {map_ms:.3f} ms), "
+    log(f"[bench] step {ms:.3f} ms (attention mean {attn_ms:.3f} / median "
+        f"{np.median(attn):.3f} / min {min(attn):.3f} ms, map {np.mean(amap):.3f} ms), "
         f"{value:.1f} effective TFLOP/s")
     extra = {
-        "attn_kernel_ms": round(attn_ms, 4),
-        "tile_map_ms": round(map_ms, 4),
+        "attn_kernel_ms": {"mean": round(attn_ms, 4), "median": round(float(np.median(attn)), 4),
+                           "min": round(min(attn), 4)},
+        "tile_map_ms": round(float(np.mean(amap)), 4),
         "retained_pairs": pairs,
         "exec_tiles_full_boundary_sink": [sum(s["exec_full"] for s in stats),
                                           sum(s["exec_boundary"] for s in stats),
                                           sum(s["exec_sink"] for s in stats)],
+        "logical_tiles_skip_full_boundary": [sum(s["skip"] for s in stats),
+                                             sum(s["full"] for s in stats),
+                                             sum(s["boundary"] for s in stats)],
     }
-    del q, k, v, o
-    if not a.no_dense and w.name == "main":
+    if not a.no_extras and w.name == "main":
+        import structured_sparse_attention_amd as svg
+        n_extra = max(3, a.steps // 4)
+        _, nattn, _, _ = time_steps(w, q, k, v, o, n_extra, 1, flags=svg.ATTN_MASK_ALL_TILES)
+        extra["naive_mask_all_tiles_ms"] = round(float(np.mean(nattn)), 4)
+        log(f"[bench] naive (mask every executed tile) {np.mean(nattn):.3f} ms")
+        wt = si.workload("tile-aligned")
+        _, tattn, _, tstats = time_steps(wt, q, k, v, o, n_extra, 1)
+        tpairs = sum(s["retained_pairs"] for s in tstats)
+        extra["tile_aligned_ms"] = round(float(np.mean(tattn)), 4)
+        extra["tile_aligned_pairs_drift"] = round(tpairs / pairs - 1.0, 5)
+        extra["tile_aligned_tflops_rounded_mask"] = round(
+            4.0 * w.head_dim * tpairs / (np.mean(tattn) * 1e-3) / 1e12, 1)
+        log(f"[bench] tile-aligned {np.mean(tattn):.3f} ms (pairs {tpairs / pairs - 1:+.3%})")
+        del q, k, v, o
         wd = si.workload("dense")
         (qd, kd, vd), _ = device_inputs(wd)
         od = torch.empty_like(qd)
-        dms, dattn, _, dstats = time_steps(wd, qd, kd, vd, od, max(3, a.steps // 4), 1)
-        extra["dense_ms"] = round(dms, 4)
-        extra["dense_attn_kernel_ms"] = round(dattn, 4)
-        extra["dense_tflops"] = round(4.0 * wd.head_dim * sum(s["retained_pairs"] for s in dstats)
-                                      / (dattn * 1e-3) / 1e12, 1)
-        extra["speedup_vs_dense"] = round(dattn / attn_ms, 3)
-        log(f"[bench] dense {dattn:.3f} ms -> sparse speed-up {dattn / attn_ms:.2f}x")
+        dms, dattn, _, dstats = time_steps(wd, qd, kd, vd, od, n_extra, 1)
+        dpairs = sum(s["retained_pairs"] for s in dstats)
+        extra["dense_attn_kernel_ms"] = round(float(np.mean(dattn)), 4)
+        extra["dense_tflops"] = round(4.0 * wd.head_dim * dpairs
+                                      / (np.mean(dattn) * 1e-3) / 1e12, 1)
+        extra["speedup_vs_dense"] = round(float(np.mean(dattn)) / attn_ms, 3)
+        log(f"[bench] dense {np.mean(dattn):.3f} ms -> sparse speed-up "
+            f"{np.mean(dattn) / attn_ms:.2f}x")
         del qd, kd, vd, od
     result = {
-        "metric": "sparse attn fwd ms + effective TFLOP/s (retained pairs) at 75,600 tok"
-                  "×10 heads×d128",
+        "metric": METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -208,11 +278,13 @@ def main():
         "config": {"workload": f"{w.name}: F={w.frames} {w.grid_h}x{w.grid_w} "
                                f"N={w.seq_len} H={w.num_heads} (5 spatial W_f={w.frame_window}, "
                                f"5 temporal W_s={w.band}, frame-0 sink) d={w.head_dim} "
-                               f"tiles {w.tile_q}x{w.tile_k} exact",
+                               f"tiles {w.tile_q}x{w.tile_k} "
+                               f"{'tile-aligned' if w.tile_aligned else 'exact'}",
                    "global_batch": 1, "seq_len": w.seq_len, "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic() if w.name == "main" else None},
         "extra": extra,
     }
     if not a.no_cpu_baseline:
