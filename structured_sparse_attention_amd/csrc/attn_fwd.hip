@@ -35,6 +35,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace svg {
 namespace {
 
@@ -42,26 +44,37 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int CK = 64;  // keys per pipeline step
 constexpr int QW = 32;  // query rows per wave
 
 template <int D, int NW>
 struct Layout {
-  static constexpr int NCH = D / 8;              // 16-byte chunks per K row
-  static constexpr int KSLOTS = NCH + 1;         // K row + one pad slot
-  static constexpr int KROW = 16 * KSLOTS;       // bytes per K row in LDS
-  static constexpr int KTILE = CK * KROW;
-  static constexpr int KLOADS = KTILE / 1024;    // 1 KiB wave-wide DMA loads
-  static constexpr int KPW = (KLOADS + NW - 1) / NW;  // DMA loads per wave
-  static constexpr int VTROW = 16 * (CK / 8 + 1);     // bytes per V^T row (one dim)
+  static constexpr int NCH = D / 8;              // 16-byte chunks per K/V row
+  static constexpr int KSLOTS = NCH + 1;         // row + one pad slot
+  static constexpr int KROW = 16 * KSLOTS;       // bytes per K/V row in LDS
+  static constexpr int KTILE = CK * KROW;        // one step's K rows (and V rows)
+  static constexpr int KLOADS = KTILE / 1024;    // 1 KiB wave-wide DMA loads per tile
+  static constexpr int VTROW = 16 * (CK / 8 + 1);  // bytes per V^T row (one dim)
   static constexpr int VTILE = D * VTROW;
-  static constexpr int BUF = KTILE + VTILE;
-  // V transpose units: 8 keys x 2 dims, one per lane and round
-  static constexpr int VUNITS = (CK / 8) * (D / 2);
-  static constexpr int VUPL = (VUNITS + NW * 64 - 1) / (NW * 64);  // units per lane
+  // One buffer: K rows | V^T | V rows.
+  static constexpr int VT_OFF = KTILE;
+  static constexpr int VR_OFF = KTILE + VTILE;
+  static constexpr int BUF = 2 * KTILE + VTILE;
+  // With eight waves, group 0 (waves 0-3) issues every HBM load and group 1
+  // (waves 4-7) transposes V; with fewer waves every wave does both.
+  static constexpr int NL = NW == 8 ? NW / 2 : NW;  // loader waves
+  static constexpr int NT = NW == 8 ? NW / 2 : NW;  // transposer waves
+  static constexpr int LPW = (KLOADS + NL - 1) / NL;  // K (and V) loads per loader wave
+  static constexpr int TCH = D * (CK / 8);            // V^T chunks (8 keys x 1 dim) per step
+  static constexpr int TPW = TCH / (NT * 64);         // chunks per transposer lane
   static_assert(KTILE % 1024 == 0, "K tile must be whole KiB");
+  static_assert(TCH % (NT * 64) == 0, "V^T chunks must split evenly over the lanes");
+  static_assert(VR_OFF % 1024 == 0, "DMA destinations must stay 1 KiB aligned");
 };
 
 struct KParams {
@@ -116,31 +129,21 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 // Descriptor of step j: `part` (0..cpt-1) of tile `kt` when `tile`, else
 // sink step js = j - (tile steps) of a temporal head: raster indices [0, a)
-// then [b, S), 64 per step, read at rows s * F.
-__device__ __forceinline__ Step make_step(const KParams& p, bool tile, bool bnd, int kt,
-                                          int part, int js, int n_s1, int sa, int sb) {
+// then [b, S), 64 per step, read at rows s * F. Both forms are computed and
+// selected, so that the step path has no branch (scalar selects only).
+__device__ __forceinline__ Step make_step(const KParams& p, int ti, int bnd, int kt, int part,
+                                          int js, int n_s1, int sa, int sb) {
+  const bool tile = ti != 0;
+  const int c0 = kt * p.BK + part * CK;
+  const int tend = min(p.N, kt * p.BK + p.BK);
+  const bool first = js < n_s1;
+  const int s0 = first ? js * CK : sb + (js - n_s1) * CK;
+  const int lim = first ? sa : p.S;
   Step s;
-  if (tile) {
-    const int c0 = kt * p.BK + part * CK;
-    const int end = min(p.N, kt * p.BK + p.BK);
-    s.base = c0;
-    s.stride = 1;
-    s.ncols = min(CK, end - c0);
-    s.pred = bnd | p.mask_all | (s.ncols < CK);
-  } else {
-    int s0, lim;
-    if (js < n_s1) {
-      s0 = js * CK;
-      lim = sa;
-    } else {
-      s0 = sb + (js - n_s1) * CK;
-      lim = p.S;
-    }
-    s.base = s0 * p.F;
-    s.stride = p.F;
-    s.ncols = min(CK, lim - s0);
-    s.pred = p.mask_all | (s.ncols < CK);
-  }
+  s.base = tile ? c0 : s0 * p.F;
+  s.stride = tile ? 1 : p.F;
+  s.ncols = min(CK, tile ? tend - c0 : lim - s0);
+  s.pred = (ti & bnd) | p.mask_all | (int)((uint32_t)(s.ncols - CK) >> 31);
   return s;
 }
 
@@ -150,126 +153,97 @@ __device__ __forceinline__ int key_row(const KParams& p, const Step& s, int r) {
   return min(s.base + (r < s.ncols ? r : 0) * s.stride, p.N - 1);
 }
 
-// Staging of one step's K (DMA into LDS) and V (dword loads into VGPRs, then
-// transposed into LDS). The (row, chunk) a lane fetches is fixed per load, so
-// its byte offset from the step's first row is computed once, for
-// consecutive rows and for rows F apart (sink steps). Full steps then pass
-// those persistent registers as they are and put everything that changes in
-// the scalar offset: no address register is rewritten while its load is in
-// flight, which would make the compiler wait for the loads before the next
-// LDS read. Short steps (ragged tails) clamp rows per lane and wait for their
-// loads at once (rare). K pad slots re-read chunk 0 of their row (in bounds,
-// never read back).
+// Staging of one step. K rows and V rows move from HBM straight into LDS
+// (buffer_load ... lds, no VGPRs), both in the same padded row layout and
+// row order (LDS row m of a 32-row block holds key sigma(m)). The (row,
+// chunk) a lane fetches in load j is fixed; its byte offset is computed per
+// step from the step's first row, row stride and column count, with rows
+// past the count clamped to the step's first row (they are masked) and
+// every row clamped into the sequence, so one branch-free sequence serves
+// full, strided (sink) and short steps. Pad slots re-read chunk 0 of their
+// row (in bounds, never read back).
+//
+// V is then transposed inside LDS once per step: each 16-lane group reads 4
+// keys x 16 dims with one ds_read_b64_tr_b16 (lane j gets dim j of the 4
+// keys), two such reads give each lane 8 keys of one dim, written as one
+// 16-byte V^T row slot. The PV product then reads V^T with ds_read_b128.
 template <int D, int NW>
 struct Stage {
   using Lt = Layout<D, NW>;
   static constexpr int ROWB = 2 * D;  // bytes per K/V row in HBM
   static constexpr int SH = D == 128 ? 8 : 7;
-  uint32_t koff[Lt::KPW], koffF[Lt::KPW];    // K: offsets, rows 1 / F apart
-  uint32_t voff[Lt::VUPL], voffF[Lt::VUPL];  // V: offset of key 0 of the unit
-  uint32_t vx[Lt::VUPL][8];                  // V: 8 keys x 2 dims in flight
+  uint32_t koff[Lt::LPW];  // row-in-step << SH | byte in row, per load
 
-  __device__ __forceinline__ void init(int wave, int lane, int F) {
+  __device__ __forceinline__ void init(int wl, int lane) {
 #pragma unroll
-    for (int i = 0; i < Lt::KPW; ++i) {
-      const int slot = (i * NW + wave) * 64 + lane;
+    for (int i = 0; i < Lt::LPW; ++i) {
+      const int slot = (i * Lt::NL + wl) * 64 + lane;
       const int prow = slot / Lt::KSLOTS, c = slot - prow * Lt::KSLOTS;
       const int r = (prow & ~31) | sigma(prow & 31);
-      const int cb = 16 * (c < Lt::NCH ? c : 0);
-      koff[i] = (uint32_t)(r * ROWB + cb);
-      koffF[i] = (uint32_t)(r * F * ROWB + cb);
-    }
-#pragma unroll
-    for (int u = 0; u < Lt::VUPL; ++u) {
-      const int unit = u * NW * 64 + wave * 64 + lane;
-      const int dp = unit % (D / 2), kg = unit / (D / 2);
-      voff[u] = (uint32_t)(8 * kg * ROWB + 4 * dp);
-      voffF[u] = (uint32_t)(8 * kg * F * ROWB + 4 * dp);
+      koff[i] = (uint32_t)(r * ROWB + 16 * (c < Lt::NCH ? c : 0));
     }
   }
 
-  __device__ __forceinline__ bool unit_ok(int u, int wave, int lane) const {
-    return Lt::VUNITS % (NW * 64) == 0 || u * NW * 64 + wave * 64 + lane < Lt::VUNITS;
-  }
-  __device__ __forceinline__ bool k_ok(int i, int wave) const {
-    return Lt::KLOADS % NW == 0 || i * NW + wave < Lt::KLOADS;
+  __device__ __forceinline__ bool k_ok(int i, int wl) const {
+    return Lt::KLOADS % Lt::NL == 0 || i * Lt::NL + wl < Lt::KLOADS;
   }
 
-  // Full step with fixed per-lane offsets `ko` / `vo` and key pitch `pitch`
-  // bytes (ROWB or F * ROWB).
-  __device__ __forceinline__ void issue_full(const char* kbase,
-                                             __amdgpu_buffer_rsrc_t vrs, uint32_t base,
-                                             uint32_t pitch, const uint32_t (&ko)[Lt::KPW],
-                                             const uint32_t (&vo)[Lt::VUPL], char* buf,
-                                             int wave, int lane) {
-    const char* kb = kbase + base;
-#pragma unroll
-    for (int i = 0; i < Lt::KPW; ++i)
-      if (k_ok(i, wave))
-        __builtin_amdgcn_global_load_lds(kb + ko[i], (lds_void*)(buf + (i * NW + wave) * 1024), 16,
-                                         0, 0);
-#pragma unroll
-    for (int u = 0; u < Lt::VUPL; ++u)
-      if (unit_ok(u, wave, lane)) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-          vx[u][r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, vo[u], base + r * pitch, 0);
-      }
+  // Load pair j (K and V rows of one 1 KiB slot) of step `s` into `buf`,
+  // without a branch: a wave that has no load j repeats its load j-1 (the
+  // same bytes to the same place).
+  __device__ __forceinline__ void load(const KParams& p, __amdgpu_buffer_rsrc_t krs,
+                                       __amdgpu_buffer_rsrc_t vrs, const Step& s, char* buf,
+                                       int wl, int j) const {
+    const bool ok = j == 0 || k_ok(j, wl);
+    const int jj = ok ? j : j - 1;
+    const uint32_t ko = koff[j > 0 && !ok ? j - 1 : j];
+    const int r = (int)(ko >> SH);
+    const int row = min(s.base + (r < s.ncols ? r : 0) * s.stride, p.N - 1);
+    const uint32_t off = (uint32_t)row * ROWB + (ko & (ROWB - 1));
+    const int at = (jj * Lt::NL + wl) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(buf + at), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(buf + Lt::VR_OFF + at), 16, off, 0,
+                                             0, 0);
   }
 
-  // Queue step `s`: K DMA into `buf`, V loads into vx.
-  __device__ __forceinline__ void issue(const KParams& p, const char* kbase,
-                                        __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                        const Step& s, char* buf, int wave, int lane) {
-    const uint32_t base = (uint32_t)s.base * ROWB;
-    if (s.ncols == CK && s.stride == 1) {
-      issue_full(kbase, vrs, base, ROWB, koff, voff, buf, wave, lane);
-    } else if (s.ncols == CK) {
-      issue_full(kbase, vrs, base, (uint32_t)p.F * ROWB, koffF, voffF, buf, wave, lane);
-    } else {
-#pragma unroll
-      for (int i = 0; i < Lt::KPW; ++i)
-        if (k_ok(i, wave)) {
-          const int r = (int)(koff[i] >> SH);
-          const uint32_t off = (uint32_t)key_row(p, s, r) * ROWB + (koff[i] & (ROWB - 1));
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              krs, (lds_void*)(buf + (i * NW + wave) * 1024), 16, off, 0, 0, 0);
-        }
-#pragma unroll
-      for (int u = 0; u < Lt::VUPL; ++u)
-        if (unit_ok(u, wave, lane)) {
-#pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            const int kr = (int)(voff[u] >> SH) + r;
-            const uint32_t off = (uint32_t)key_row(p, s, kr) * ROWB + (voff[u] & (ROWB - 1));
-            vx[u][r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, off, 0, 0);
-          }
-        }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the temporaries are free again
-    }
+  // V rows of `src` -> V^T of `dst` (this transposer wave's share). Chunk
+  // c = (t * NT + wt) * 64 + lane is dim c % D of key group c / D; a 16-lane
+  // group covers 16 consecutive dims of one key group. Addresses split into a
+  // per-lane part (fixed) and a wave-uniform part per pass.
+  struct TrLane {
+    int rd, wr;
+  };
+  __device__ __forceinline__ static TrLane tr_lane(int lane) {
+    const int q = lane >> 4, jj = lane & 15;
+    return {(jj >> 2) * Lt::KROW + 2 * (16 * q + 4 * (jj & 3)), (16 * q + jj) * Lt::VTROW};
   }
-
-  // Transpose the staged V (after its loads completed) into V^T in `buf`.
-  __device__ __forceinline__ void store_vt(char* buf, int wave, int lane) const {
+  // uniform part of pass t: read offsets of keys 8g..8g+3 and 8g+4..8g+7
+  // (LDS rows sigma(key): sigma is its own inverse) and the write offset
+  __device__ __forceinline__ static int tr_rd(int wt, int t, int half) {
+    const int u = t * Lt::NT + wt, dd = (u % (D / 64)) * 64, g = u / (D / 64);
+    const int pr = 32 * (g >> 2) + sigma(8 * (g & 3) + 4 * half);
+    return Lt::VR_OFF + pr * Lt::KROW + 2 * dd;
+  }
+  __device__ __forceinline__ static int tr_wr(int wt, int t) {
+    const int u = t * Lt::NT + wt, dd = (u % (D / 64)) * 64, g = u / (D / 64);
+    return Lt::VT_OFF + dd * Lt::VTROW + 16 * g;
+  }
+  __device__ __forceinline__ static i16x8 tr_read(const char* src, const TrLane& tl, int wt,
+                                                  int t) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(src + tr_rd(wt, t, 0) + tl.rd));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(src + tr_rd(wt, t, 1) + tl.rd));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  __device__ __forceinline__ static void tr_write(char* dst, const TrLane& tl, int wt, int t,
+                                                  const i16x8& x) {
+    *(i16x8*)(dst + tr_wr(wt, t) + tl.wr) = x;
+  }
+  __device__ __forceinline__ static void transpose(const char* src, char* dst, const TrLane& tl,
+                                                   int wt) {
 #pragma unroll
-    for (int u = 0; u < Lt::VUPL; ++u) {
-      if (unit_ok(u, wave, lane)) {
-        const int unit = u * NW * 64 + wave * 64 + lane;
-        const int dp = unit % (D / 2), kg = unit / (D / 2);
-        uint4 lo, hi;  // dims 2dp and 2dp+1, keys 8kg .. 8kg+7
-        lo.x = __builtin_amdgcn_perm(vx[u][1], vx[u][0], 0x05040100u);
-        lo.y = __builtin_amdgcn_perm(vx[u][3], vx[u][2], 0x05040100u);
-        lo.z = __builtin_amdgcn_perm(vx[u][5], vx[u][4], 0x05040100u);
-        lo.w = __builtin_amdgcn_perm(vx[u][7], vx[u][6], 0x05040100u);
-        hi.x = __builtin_amdgcn_perm(vx[u][1], vx[u][0], 0x07060302u);
-        hi.y = __builtin_amdgcn_perm(vx[u][3], vx[u][2], 0x07060302u);
-        hi.z = __builtin_amdgcn_perm(vx[u][5], vx[u][4], 0x07060302u);
-        hi.w = __builtin_amdgcn_perm(vx[u][7], vx[u][6], 0x07060302u);
-        char* vt = buf + Lt::KTILE + 2 * dp * Lt::VTROW + 16 * kg;
-        *(uint4*)vt = lo;
-        *(uint4*)(vt + Lt::VTROW) = hi;
-      }
-    }
+    for (int t = 0; t < Lt::TPW; ++t) tr_write(dst, tl, wt, t, tr_read(src, tl, wt, t));
   }
 };
 
@@ -300,33 +274,35 @@ struct Cursor {
     e_cur = load(0, lane);
     e_nxt = load(1, lane);
   }
-  // descriptor of the current step; the cursor moves one step on
+  // descriptor of the current step; the cursor moves one step on (only the
+  // refill of the 64-entry window branches)
   __device__ __forceinline__ Step take(const KParams& p, int lane) {
-    const bool tile = e < n_tiles;
-    int kt = 0;
-    if (tile) {
-      if ((e >> 6) != chunk) {  // entries are visited in order: next chunk
-        e_cur = e_nxt;
-        ++chunk;
-        e_nxt = load(chunk + 1, lane);
-      }
-      kt = __builtin_amdgcn_readlane(e_cur, __builtin_amdgcn_readfirstlane(e & 63));
+    // (integer arithmetic rather than selects on comparisons, which the
+    // compiler would widen through vector registers)
+    const int ti = (int)((uint32_t)(e - n_tiles) >> 31);     // e < n_tiles
+    const int bnd = (int)((uint32_t)(n_full - 1 - e) >> 31);  // e >= n_full
+    if (ti && (e >> 6) != chunk) {  // entries are visited in order: next chunk
+      e_cur = e_nxt;
+      ++chunk;
+      e_nxt = load(chunk + 1, lane);
     }
-    const Step st = make_step(p, tile, e >= n_full, kt, part, js, n_s1, sa, sb);
-    if (tile) {
-      if (++part == p.cpt) {
-        part = 0;
-        ++e;
-      }
-    } else {
-      ++js;
-    }
+    const int kt = __builtin_amdgcn_readlane(e_cur, __builtin_amdgcn_readfirstlane(e & 63));
+    const Step st = make_step(p, ti, bnd, kt, part, js, n_s1, sa, sb);
+    const int last = 1 - min(1, p.cpt - part - 1);           // part + 1 == cpt
+    e += ti * last;
+    part += ti * (1 - last * (part + 1));                    // part + 1, or 0 after the last
+    js += 1 - ti;
     return st;
   }
 };
 
 // vmcnt(0), as an instruction the compiler accounts for
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Workgroup barrier after this wave's LDS operations completed. Unlike
+// __syncthreads() it does not also wait for outstanding global loads.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
@@ -335,7 +311,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
   constexpr int NS = 2 * (D / 16);  // MFMAs of S^T per step: (d-step, key block)
   constexpr int NDB = D / 32;       // 32-row blocks of O^T
   constexpr int NPV = 4 * NDB;      // MFMAs of O^T per step: (16-key step, d block)
+  constexpr int NM = NPV + NS;      // MFMAs of one M phase
   constexpr int PD = 4;             // LDS operand prefetch depth, in MFMAs
+  constexpr int LS = NM / Lt::LPW < 3 ? (NM / Lt::LPW < 1 ? 1 : NM / Lt::LPW) : 3;  // MFMAs per load pair
+  // MFMAs between a transpose pass's reads and its write
+  constexpr int TRW = NM - 2 - 6 * (Lt::TPW - 1) < 11 ? NM - 2 - 6 * (Lt::TPW - 1) : 11;
+  // Eight waves form two groups, one wave of each per SIMD, that alternate
+  // between the MFMA phase and the softmax phase.
+  constexpr bool PP = NW == 8;
   constexpr float NEG_INF = -__builtin_huge_valf();
   __shared__ __attribute__((aligned(1024))) char buf0[Lt::BUF];
   __shared__ __attribute__((aligned(1024))) char buf1[Lt::BUF];
@@ -343,6 +326,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane >> 5, l32 = lane & 31;
+  const int grp = PP && wave >= NW / 2 ? 1 : 0;
 
   const int L = xcd_remap(blockIdx.x, p.total_wg);
   const int row = L / p.nsub, sub = L - row * p.nsub;
@@ -361,22 +345,31 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
   const size_t head_off = (size_t)h * p.N * D;
   const uint16_t* Qh = p.q + head_off;
   const int head_bytes = p.N * D * 2;
-  const char* kbytes = (const char*)(p.k + head_off);
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + head_off), (short)0, head_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + head_off), (short)0, head_bytes, 0x00020000);
 
+  // Group 0 (every wave with fewer than eight) issues the HBM loads, group 1
+  // (every wave with fewer than eight) transposes V.
+  const bool loader = !PP || grp == 0;
+  const int wl = wave, wt = PP ? wave - NW / 2 : wave;
+  const typename Stage<D, NW>::TrLane tl = Stage<D, NW>::tr_lane(lane);
   Stage<D, NW> stg;
-  stg.init(wave, lane, p.F);
-  // Start the first K/V transfer before anything else.
+  if (loader) stg.init(wl, lane);
+  // Stage 0 holds the first step's K and V rows; its V^T area holds zeros,
+  // which the first MFMA phase multiplies by P = 0.
   Cursor cur_pos;
   cur_pos.init(p.entries + ebeg, n_tiles, n_full, n_s1, sa, sb, lane);
-  Step nxt = {0, 1, 0, 0};
+  Step st_t = {0, 1, 0, 0};
   if (n_steps > 0) {
-    nxt = cur_pos.take(p, lane);
-    stg.issue(p, kbytes, krs, vrs, nxt, buf0, wave, lane);
+    st_t = cur_pos.take(p, lane);
+    if (loader)
+#pragma unroll
+      for (int j = 0; j < Lt::LPW; ++j) stg.load(p, krs, vrs, st_t, buf0, wl, j);
   }
+  for (int off = threadIdx.x * 16; off < Lt::VTILE; off += NW * 64 * 16)
+    *(uint4*)(buf0 + Lt::VT_OFF + off) = make_uint4(0, 0, 0, 0);
 
   // ---- Q fragments (B operand of S^T = K Q^T) and this lane's mask bounds.
   const int q = wg_q + wave * QW + l32;
@@ -425,6 +418,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
   float m_ref = NEG_INF, l_sum = 0.f;
+  f32x16 s[2];   // S^T of a step, from its MFMA phase to its softmax phase
+  bf16x8 pf[4];  // P^T of a step, from its softmax phase to the next MFMA phase
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) pf[kk] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
 
   // Per-lane LDS read bases (the rest of every address is a constant).
   const int k_lane = l32 * Lt::KROW + 16 * hl;
@@ -439,62 +436,51 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
     const int kk = i / NDB, db = i % NDB;
     return *(const bf16x8*)(vb + 32 * db * Lt::VTROW + 32 * kk);
   };
+  auto opread = [&](const char* kb, const char* vb, int i) __attribute__((always_inline)) {
+    return i < NPV ? vread(vb, i) : kread(kb, i - NPV);
+  };
 
-  if (n_steps > 0) {
-    wait_vmem();
-    stg.store_vt(buf0, wave, lane);
-  }
-  __syncthreads();
-
-  // One step: compute on `cbuf` while the next step's K/V stream towards
-  // `nbuf`. The two buffers are distinct LDS objects and the loop is unrolled
-  // by two, so the compiler can tell that the reads of this step never alias
-  // the DMA in flight and does not wait for it before reading.
-  auto run_step = [&](const char* cbuf, char* nbuf, int j) __attribute__((always_inline)) {
-    const Step cur = nxt;
-    const bool more = j + 1 < n_steps;
-    if (more) {
-      nxt = cur_pos.take(p, lane);
-      stg.issue(p, kbytes, krs, vrs, nxt, nbuf, wave, lane);
-    }
-
-    // S^T = K Q^T: 64 keys x 32 queries, K operands read PD MFMAs ahead; the
-    // first V operands load under the last MFMAs.
-    const char* kb = cbuf + k_lane;
-    const char* vb = cbuf + v_lane;
-    f32x16 s[2];
+  // MFMA phase on the stage in `cb`: O^T += V^T P^T for the previous step,
+  // then S^T = K Q^T for this one; operands read PD MFMAs ahead. The wave is
+  // idle between its MFMAs, so other memory work rides along: side.at(i)
+  // emits it after MFMA i and side.pattern(i) places it in the schedule.
+  auto mphase = [&](const char* cb, auto&& side) __attribute__((always_inline)) {
+    const char* kb = cb + k_lane;
+    const char* vb = cb + v_lane;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[kb2][v] = 0.f;
-    bf16x8 ka[PD];
+    bf16x8 a[PD];
 #pragma unroll
-    for (int i = 0; i < PD; ++i) ka[i] = kread(kb, i);
+    for (int i = 0; i < PD; ++i) a[i] = opread(kb, vb, i);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const bf16x8 a = ka[i % PD];
-      if (i + PD < NS) ka[i % PD] = kread(kb, i + PD);
-      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i >> 1], s[i & 1], 0, 0, 0);
+    for (int i = 0; i < NM; ++i) {
+      const bf16x8 x = a[i % PD];
+      if (i + PD < NM) a[i % PD] = opread(kb, vb, i + PD);
+      if (i < NPV) {
+        o[i % NDB] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, pf[i / NDB], o[i % NDB], 0, 0, 0);
+      } else {
+        const int k = i - NPV;
+        s[k & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, qf[k >> 1], s[k & 1], 0, 0, 0);
+      }
+      side.at(i);
     }
-    bf16x8 va[PD];
-#pragma unroll
-    for (int i = 0; i < PD; ++i) va[i] = vread(vb, i);
     // Keep the reads ahead of their MFMAs (the default schedule assumes a
-    // far shorter LDS latency): transfers first, PD K reads, one K read per
-    // MFMA, then the first V operands under the last MFMAs.
-    __builtin_amdgcn_sched_group_barrier(0x020, Lt::KPW + 8 * Lt::VUPL, 0);
+    // far shorter LDS latency).
     __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
 #pragma unroll
-    for (int i = 0; i < NS - PD; ++i) {
+    for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i + PD < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      side.pattern(i);
     }
-#pragma unroll
-    for (int i = 0; i < PD; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
+  };
 
+  // Softmax phase of step `cur`: mask, lazy running maximum, P^T = exp2(...)
+  // in bf16 and the row sum.
+  auto vphase = [&](const Step& cur) __attribute__((always_inline)) {
     // mask: column limit of short steps, head predicate on boundary tiles.
     // The keep bits of the lane's 32 keys are built in a rolled loop (small
     // code, rare path), then applied.
@@ -513,17 +499,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
         for (int v = 0; v < 16; ++v)
           if (!((keep >> (16 * kb2 + v)) & 1u)) s[kb2][v] = NEG_INF;
     }
-
-    // online softmax, lazy rescaling
     float mx = NEG_INF;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb2][v]);
     {
-      float a, b;
-      halves(mx, a, b);
-      mx = fmaxf(a, b);
+      float x0, x1;
+      halves(mx, x0, x1);
+      mx = fmaxf(x0, x1);
     }
     const bool need = mx > m_ref + p.thr;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -539,7 +523,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
         for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
     }
     const float mc = m_ref == NEG_INF ? 0.f : m_ref * p.c;
-    bf16x8 pf[4];
+    // (the row sum uses plain adds: v_dot2 cannot issue while the partner
+    // wave's MFMAs run)
+    float ls[2] = {0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       uint32_t w[4];
@@ -548,29 +534,110 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
         const int v = 8 * (kk & 1) + 2 * t;
         const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][v], p.c, -mc));
         const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][v + 1], p.c, -mc));
-        l_sum += e0 + e1;
+        ls[t & 1] += e0 + e1;
         w[t] = pack_bf16(e0, e1);
       }
       pf[kk] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
     }
-
-    // O^T += V^T P^T, V operands read PD MFMAs ahead
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      const bf16x8 a = va[i % PD];
-      if (i + PD < NPV) va[i % PD] = vread(vb, i + PD);
-      o[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[i / NDB], o[i % NDB], 0, 0, 0);
-    }
-
-    // the next step's V arrived during this step: transpose it into LDS
-    wait_vmem();
-    if (more) stg.store_vt(nbuf, wave, lane);
-    __syncthreads();
+    l_sum += ls[0] + ls[1];
   };
 
-  for (int j = 0; j < n_steps; j += 2) {
-    run_step(buf0, buf1, j);
-    if (j + 1 < n_steps) run_step(buf1, buf0, j + 1);
+  if (n_steps > 0) {
+    wait_vmem();
+    __syncthreads();  // stage 0 and the zero V^T visible to every wave
+
+    // Iteration t works on the buffer `cb` that holds the K rows of step t,
+    // V^T of step t-1 and the V rows of step t, and fills `nb` for step t+1.
+    // Group 0 runs the MFMA phase of step t (PV of step t-1, S^T of step t)
+    // with the loads of the K and V rows of step t+1 into `nb` woven in,
+    // then the softmax of step t. Group 1 runs the softmax of step t-1, then
+    // the MFMA phase of step t with the transpose of V of step t into V^T of
+    // `nb` woven in. The softmax phases carry no memory work, and the waves
+    // of a SIMD alternate: one runs its MFMAs while the other runs its
+    // softmax. A barrier separates the two phases, another closes the
+    // iteration once the loads have landed. Iteration n_steps only finishes
+    // the last PV product (its S^T reads K rows that are not loaded and is
+    // never used). One loop per group (the group is a compile-time constant
+    // in each), so that the two phase orders are never merged.
+    auto run = [&](auto grp_c) __attribute__((always_inline)) {
+      constexpr int G = decltype(grp_c)::value;
+      Step st_prev = st_t;
+      auto iter = [&](const char* cb, char* nb, int t) __attribute__((always_inline)) {
+        const bool more = t + 1 < n_steps;
+        const bool has_v = t < n_steps;
+        Step st_next = st_t;
+        if (more) st_next = cur_pos.take(p, lane);
+        if constexpr (G == 0) {
+          // One K+V load pair every LS-th MFMA (every third when there are
+          // few). After the last step they fetch rows of the last step again
+          // into a stage nobody reads.
+          struct DmaSide {
+            const KParams& p;
+            const Stage<D, NW>& stg;
+            __amdgpu_buffer_rsrc_t krs, vrs;
+            const Step& st;
+            char* nb;
+            int wl;
+            __device__ __forceinline__ void at(int i) const {
+              if (i % LS == 0 && i / LS < Lt::LPW) stg.load(p, krs, vrs, st, nb, wl, i / LS);
+            }
+            __device__ __forceinline__ void pattern(int i) const {
+              if (i % LS == 0 && i / LS < Lt::LPW) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            }
+          };
+          static_assert(Lt::LPW <= NM, "every load pair needs an MFMA slot");
+          if (!PP) Stage<D, NW>::transpose(cb, nb, tl, wt);
+          mphase(cb, DmaSide{p, stg, krs, vrs, st_next, nb, wl});
+          if (PP) __builtin_amdgcn_s_barrier();
+          if (has_v) vphase(st_t);
+        } else {
+          if (t > 0) vphase(st_prev);
+          __builtin_amdgcn_s_barrier();
+          // Transpose pass j: reads after MFMA 6j+1, write TRW MFMAs later (the
+          // reads wait behind the operand reads). After the last step it fills
+          // a V^T nobody reads.
+          struct TrSide {
+            const char* cb;
+            char* nb;
+            const typename Stage<D, NW>::TrLane& tl;
+            int wt;
+            i16x8 (&buf)[Lt::TPW];
+            __device__ __forceinline__ void at(int i) const {
+#pragma unroll
+              for (int j = 0; j < Lt::TPW; ++j) {
+                if (i == 6 * j + 1) buf[j] = Stage<D, NW>::tr_read(cb, tl, wt, j);
+                if (i == 6 * j + 1 + TRW) Stage<D, NW>::tr_write(nb, tl, wt, j, buf[j]);
+              }
+            }
+            __device__ __forceinline__ void pattern(int i) const {
+#pragma unroll
+              for (int j = 0; j < Lt::TPW; ++j) {
+                if (i == 6 * j + 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                if (i == 6 * j + 1 + TRW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+              }
+            }
+          };
+          static_assert(TRW >= 4 || !PP, "transpose passes must fit the phase");
+          i16x8 trbuf[Lt::TPW];
+          mphase(cb, TrSide{cb, nb, tl, wt, trbuf});
+        }
+        // (pinned here: the scheduler would otherwise hoist the wait into
+        // the phases above)
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmem();
+        barrier_lds();
+        st_prev = st_t;
+        st_t = st_next;
+      };
+      for (int t = 0; t <= n_steps; t += 2) {
+        iter(buf0, buf1, t);
+        if (t + 1 <= n_steps) iter(buf1, buf0, t + 1);
+      }
+    };
+    if (grp == 0)
+      run(std::integral_constant<int, 0>{});
+    else
+      run(std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: O = O^T / l, bf16 (round to nearest even)
