@@ -18,19 +18,28 @@
 // when a new maximum exceeds the reference by more than 8 in log2 units, so
 // exp2 values stay below 2^8 and the final O / l is unchanged.
 //
-// Staging. The LDS issues about one wave-wide read every six cycles whatever
-// its width, so both MFMA operands are read with ds_read_b128 (16 per step
-// each for K and V^T). K moves from HBM straight into LDS (buffer_load ...
-// lds, no VGPRs). V is stored transposed: each lane loads 8 keys x 2 dims
-// with dword buffer loads, transposes them with v_perm_b32 and writes two
-// 16-byte V^T rows; strided sink keys take the same path. Both are
-// double-buffered: the transfers for step j+1 are in flight while step j
-// computes. LDS rows are padded (K 272 bytes, V^T 144) so that 16 lanes
-// reading 16 consecutive rows at one column hit 16 distinct 4-bank groups of
-// the 64 banks, and every read address is a per-lane base plus a constant.
-// K rows are stored in the order the S^T accumulator layout needs for P^T to
-// be the B operand of the PV product as it stands. Workgroups are remapped so
-// that consecutive Q tiles of a head run on the same XCD and share its L2.
+// Schedule. A wave cannot overlap its own MFMAs with its own VALU work, but
+// the two waves of a SIMD can overlap each other's. With eight waves the
+// workgroup forms two groups, one wave of each per SIMD, and every step has
+// two phases separated by a barrier: while group 0 runs the MFMA phase of
+// step t (PV of step t-1, then S^T of step t), group 1 runs the softmax of
+// step t-1; then group 0 runs the softmax of step t while group 1 runs its
+// MFMA phase. All memory work rides in the wave that is otherwise idle
+// between MFMAs: group 0 issues the next step's loads inside its MFMA phase,
+// group 1 transposes V (reads during its softmax, writes during its MFMA
+// phase). With fewer waves every wave runs both phases in turn.
+//
+// Staging. K rows and V rows move from HBM straight into LDS (buffer_load
+// ... lds, no VGPRs), one step ahead, into two buffers used in turn. V is
+// transposed once per step inside LDS (ds_read_b64_tr_b16, then 16-byte
+// writes) so that both MFMA operands are read with ds_read_b128: the LDS
+// issues about one wave-wide read every four cycles whatever its width. LDS
+// rows are padded (272 bytes, and 144 for V^T) so that 16 lanes reading 16
+// consecutive rows at one column hit 16 distinct 4-bank groups of the 64
+// banks. K rows are stored in the order the S^T accumulator layout needs for
+// P^T to be the B operand of the PV product as it stands. Workgroups are
+// remapped so that consecutive Q tiles of a head run on the same XCD and
+// share its L2.
 #include "svg_internal.hpp"
 
 #include <math.h>
@@ -274,18 +283,23 @@ struct Cursor {
     e_cur = load(0, lane);
     e_nxt = load(1, lane);
   }
-  // descriptor of the current step; the cursor moves one step on (only the
-  // refill of the 64-entry window branches)
-  __device__ __forceinline__ Step take(const KParams& p, int lane) {
-    // (integer arithmetic rather than selects on comparisons, which the
-    // compiler would widen through vector registers)
-    const int ti = (int)((uint32_t)(e - n_tiles) >> 31);     // e < n_tiles
-    const int bnd = (int)((uint32_t)(n_full - 1 - e) >> 31);  // e >= n_full
-    if (ti && (e >> 6) != chunk) {  // entries are visited in order: next chunk
+  // Refill the window when the next step starts a new 64-entry chunk (the
+  // only branch of the cursor; rare).
+  __device__ __forceinline__ void refill(int lane) {
+    if (e < n_tiles && (e >> 6) != chunk) {  // entries are visited in order
       e_cur = e_nxt;
       ++chunk;
       e_nxt = load(chunk + 1, lane);
     }
+  }
+  // Descriptor of the next step; the cursor moves one step on. Branch-free,
+  // so that it can run between the MFMAs of a phase. Past the last step it
+  // yields descriptors of rows that are never used.
+  __device__ __forceinline__ Step next(const KParams& p) {
+    // (integer arithmetic rather than selects on comparisons, which the
+    // compiler would widen through vector registers)
+    const int ti = (int)((uint32_t)(e - n_tiles) >> 31);     // e < n_tiles
+    const int bnd = (int)((uint32_t)(n_full - 1 - e) >> 31);  // e >= n_full
     const int kt = __builtin_amdgcn_readlane(e_cur, __builtin_amdgcn_readfirstlane(e & 63));
     const Step st = make_step(p, ti, bnd, kt, part, js, n_s1, sa, sb);
     const int last = 1 - min(1, p.cpt - part - 1);           // part + 1 == cpt
@@ -301,7 +315,18 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // Workgroup barrier after this wave's LDS operations completed. Unlike
 // __syncthreads() it does not also wait for outstanding global loads.
 __device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// Barrier between the two phases of a step. The scheduler must not move
+// work across it: a barrier orders memory operations only, and softmax work
+// sunk into the MFMA phase (or the reverse) would run on the wave's own
+// VALU beside its MFMAs instead of beside the partner wave's.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D, int NW>
@@ -314,8 +339,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
   constexpr int NM = NPV + NS;      // MFMAs of one M phase
   constexpr int PD = 4;             // LDS operand prefetch depth, in MFMAs
   constexpr int LS = NM / Lt::LPW < 3 ? (NM / Lt::LPW < 1 ? 1 : NM / Lt::LPW) : 3;  // MFMAs per load pair
-  // MFMAs between a transpose pass's reads and its write
-  constexpr int TRW = NM - 2 - 6 * (Lt::TPW - 1) < 11 ? NM - 2 - 6 * (Lt::TPW - 1) : 11;
   // Eight waves form two groups, one wave of each per SIMD, that alternate
   // between the MFMA phase and the softmax phase.
   constexpr bool PP = NW == 8;
@@ -363,7 +386,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
   cur_pos.init(p.entries + ebeg, n_tiles, n_full, n_s1, sa, sb, lane);
   Step st_t = {0, 1, 0, 0};
   if (n_steps > 0) {
-    st_t = cur_pos.take(p, lane);
+    st_t = cur_pos.next(p);
     if (loader)
 #pragma unroll
       for (int j = 0; j < Lt::LPW; ++j) stg.load(p, krs, vrs, st_t, buf0, wl, j);
@@ -543,6 +566,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
   };
 
   if (n_steps > 0) {
+    cur_pos.refill(lane);
+    Step st_next = cur_pos.next(p);  // step 1 (rows never used when there is none)
     wait_vmem();
     __syncthreads();  // stage 0 and the zero V^T visible to every wave
 
@@ -563,10 +588,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
       constexpr int G = decltype(grp_c)::value;
       Step st_prev = st_t;
       auto iter = [&](const char* cb, char* nb, int t) __attribute__((always_inline)) {
-        const bool more = t + 1 < n_steps;
         const bool has_v = t < n_steps;
-        Step st_next = st_t;
-        if (more) st_next = cur_pos.take(p, lane);
+        // The descriptor of step t+2 is computed off the critical path: by
+        // group 0 between the MFMAs of its MFMA phase, by group 1 with its
+        // softmax (scalar work interleaved with MFMAs would delay them).
+        cur_pos.refill(lane);
+        Step st_nn;
         if constexpr (G == 0) {
           // One K+V load pair every LS-th MFMA (every third when there are
           // few). After the last step they fetch rows of the last step again
@@ -587,39 +614,40 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
           };
           static_assert(Lt::LPW <= NM, "every load pair needs an MFMA slot");
           if (!PP) Stage<D, NW>::transpose(cb, nb, tl, wt);
+          st_nn = cur_pos.next(p);
           mphase(cb, DmaSide{p, stg, krs, vrs, st_next, nb, wl});
-          if (PP) __builtin_amdgcn_s_barrier();
+          if (PP) phase_barrier();
           if (has_v) vphase(st_t);
         } else {
+          // The transpose reads its V rows at the start of the softmax phase
+          // (the VALU-bound phase issues them almost for free) and writes V^T
+          // during the MFMA phase, long after the reads have landed, so no
+          // write waits. After the last step it fills a V^T nobody reads.
+          i16x8 trbuf[Lt::TPW];
+#pragma unroll
+          for (int j = 0; j < Lt::TPW; ++j) trbuf[j] = Stage<D, NW>::tr_read(cb, tl, wt, j);
+          st_nn = cur_pos.next(p);
           if (t > 0) vphase(st_prev);
-          __builtin_amdgcn_s_barrier();
-          // Transpose pass j: reads after MFMA 6j+1, write TRW MFMAs later (the
-          // reads wait behind the operand reads). After the last step it fills
-          // a V^T nobody reads.
+          phase_barrier();
+          // write j after MFMA 4j+2
           struct TrSide {
-            const char* cb;
             char* nb;
             const typename Stage<D, NW>::TrLane& tl;
             int wt;
-            i16x8 (&buf)[Lt::TPW];
+            const i16x8 (&buf)[Lt::TPW];
             __device__ __forceinline__ void at(int i) const {
 #pragma unroll
-              for (int j = 0; j < Lt::TPW; ++j) {
-                if (i == 6 * j + 1) buf[j] = Stage<D, NW>::tr_read(cb, tl, wt, j);
-                if (i == 6 * j + 1 + TRW) Stage<D, NW>::tr_write(nb, tl, wt, j, buf[j]);
-              }
+              for (int j = 0; j < Lt::TPW; ++j)
+                if (i == 4 * j + 2) Stage<D, NW>::tr_write(nb, tl, wt, j, buf[j]);
             }
             __device__ __forceinline__ void pattern(int i) const {
 #pragma unroll
-              for (int j = 0; j < Lt::TPW; ++j) {
-                if (i == 6 * j + 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                if (i == 6 * j + 1 + TRW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-              }
+              for (int j = 0; j < Lt::TPW; ++j)
+                if (i == 4 * j + 2) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
             }
           };
-          static_assert(TRW >= 4 || !PP, "transpose passes must fit the phase");
-          i16x8 trbuf[Lt::TPW];
-          mphase(cb, TrSide{cb, nb, tl, wt, trbuf});
+          static_assert(4 * Lt::TPW + 2 < NM || !PP, "transpose writes must fit the phase");
+          mphase(cb, TrSide{nb, tl, wt, trbuf});
         }
         // (pinned here: the scheduler would otherwise hoist the wait into
         // the phases above)
@@ -628,6 +656,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
         barrier_lds();
         st_prev = st_t;
         st_t = st_next;
+        st_next = st_nn;
       };
       for (int t = 0; t <= n_steps; t += 2) {
         iter(buf0, buf1, t);
