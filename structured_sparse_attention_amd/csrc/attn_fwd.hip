@@ -505,17 +505,35 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
   // in bf16 and the row sum.
   auto vphase = [&](const Step& cur) __attribute__((always_inline)) {
     // mask: column limit of short steps, head predicate on boundary tiles.
-    // The keep bits of the lane's 32 keys are built in a rolled loop (small
-    // code, rare path), then applied.
+    // Key kl of the step sits at row base + kl * stride, so the window, the
+    // spatial sink and the column limit are intervals of kl and the strided
+    // sink (rows that are multiples of F) is a pattern shared by the wave:
+    // the step's 64 keep bits form one 64-bit mask per lane, of which the
+    // lane keeps the bytes of its own keys (8-key groups 2c + hl).
     if (cur.pred) {
-      uint32_t keep = 0;
-#pragma nounroll
-      for (int e = 0; e < 32; ++e) {
-        const int kl = 32 * (e >> 4) + 16 * ((e >> 3) & 1) + 8 * hl + (e & 7);
-        const int kp = cur.base + kl * cur.stride;
-        const bool in = (kp >= wlo && kp < whi) || kp < slim || (msink && kp % p.F == 0);
-        keep |= (uint32_t)(kl < cur.ncols && in) << e;
+      const int sd = cur.stride;
+      auto kl_at = [&](int x) __attribute__((always_inline)) {  // first key at or past row x
+        const int d = x - cur.base;
+        int k = 0;
+        if (d > 0) k = sd == 1 ? d : (d + sd - 1) / sd;
+        return min(k, 64);
+      };
+      auto ge = [](int a) __attribute__((always_inline)) {  // keys a..63
+        return a >= 64 ? 0ull : ~0ull << a;
+      };
+      uint64_t m = (ge(kl_at(wlo)) & ~ge(kl_at(whi))) | ~ge(kl_at(slim));
+      if (msink) {
+        uint64_t pat = 0;
+        if (sd == 1) {
+          for (int k = (p.F - cur.base % p.F) % p.F; k < 64; k += p.F) pat |= 1ull << k;
+        } else if (cur.base % p.F == 0) {
+          pat = ~0ull;  // a stride of F keeps the row residue mod F
+        }
+        m |= pat;
       }
+      m &= ~ge(max(cur.ncols, 0));
+      const uint32_t keep = __builtin_amdgcn_perm((uint32_t)(m >> 32), (uint32_t)m,
+                                                  hl ? 0x07050301u : 0x06040200u);
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
