@@ -39,7 +39,8 @@
 // banks. K rows are stored in the order the S^T accumulator layout needs for
 // P^T to be the B operand of the PV product as it stands. Workgroups are
 // remapped so that consecutive Q tiles of a head run on the same XCD and
-// share its L2.
+// share its L2, in blocks dealt out in rounds so that the XCDs stay
+// balanced.
 #include "svg_internal.hpp"
 
 #include <math.h>
@@ -118,9 +119,19 @@ __device__ __forceinline__ int sigma(int m) {
   return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
 }
 
+// Logical workgroup of launch index i (T workgroups). The hardware deals
+// launch indices round-robin over the 8 XCDs; XCD x then takes blocks of XB
+// consecutive logical workgroups (consecutive Q tiles of a head, which share
+// their KV tiles in the XCD's L2) in rounds, block 8r + x in round r, so that
+// every XCD sees a mix of heads and finishes with the others. Workgroups past
+// the last full round are split into contiguous runs, one per XCD.
+constexpr int XB = 16;
 __device__ __forceinline__ int xcd_remap(int i, int T) {
-  const int x = i & 7, j = i >> 3, per = T >> 3, rem = T & 7;
-  return x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+  const int x = i & 7, j = i >> 3;
+  const int J = XB * (T / (8 * XB));  // per XCD, in full rounds
+  if (j < J) return ((j / XB) * 8 + x) * XB + j % XB;
+  const int jr = j - J, Tr = T - 8 * J, per = Tr >> 3, rem = Tr & 7;
+  return 8 * J + (x < rem ? x * (per + 1) + jr : rem * (per + 1) + (x - rem) * per + jr);
 }
 
 // Values of this lane and of lane ^ 32.
@@ -540,18 +551,45 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
         for (int v = 0; v < 16; ++v)
           if (!((keep >> (16 * kb2 + v)) & 1u)) s[kb2][v] = NEG_INF;
     }
-    float mx = NEG_INF;
+    // P^T = exp2(S^T c - m_ref c) in bf16 and this lane's part of the row sum
+    // (plain adds: v_dot2 cannot issue while the partner wave's MFMAs run)
+    auto expo = [&]() __attribute__((always_inline)) {
+      const float mc = m_ref == NEG_INF ? 0.f : m_ref * p.c;
+      float ls[2] = {0.f, 0.f};
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kk = 0; kk < 4; ++kk) {
+        uint32_t w[4];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb2][v]);
-    {
-      float x0, x1;
-      halves(mx, x0, x1);
-      mx = fmaxf(x0, x1);
-    }
-    const bool need = mx > m_ref + p.thr;
-    if (__builtin_amdgcn_ballot_w64(need)) {
+        for (int t = 0; t < 4; ++t) {
+          const int v = 8 * (kk & 1) + 2 * t;
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][v], p.c, -mc));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][v + 1], p.c, -mc));
+          ls[t & 1] += e0 + e1;
+          w[t] = pack_bf16(e0, e1);
+        }
+        pf[kk] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+      }
+      return ls[0] + ls[1];
+    };
+    // The lazy reference m_ref only has to keep every value at most 2^8. A
+    // partial row sum of at most 2^8 (finite) proves that for the lane's
+    // keys, so the row maximum is needed only when some lane's sum exceeds
+    // it or no reference exists yet: then the maximum over both halves of
+    // the row is taken, O and the row sum are rescaled when it grew by more
+    // than 8 in log2 units, and the values are computed again.
+    float ls = expo();
+    if (__builtin_amdgcn_ballot_w64(!(ls <= 256.f) || m_ref == NEG_INF)) {
+      float mx = NEG_INF;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb2][v]);
+      {
+        float x0, x1;
+        halves(mx, x0, x1);
+        mx = fmaxf(x0, x1);
+      }
+      const bool need = mx > m_ref + p.thr;
       float alpha = 1.f;
       if (need) {
         alpha = __builtin_amdgcn_exp2f((m_ref - mx) * p.c);
@@ -562,25 +600,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+      ls = expo();
     }
-    const float mc = m_ref == NEG_INF ? 0.f : m_ref * p.c;
-    // (the row sum uses plain adds: v_dot2 cannot issue while the partner
-    // wave's MFMAs run)
-    float ls[2] = {0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      uint32_t w[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int v = 8 * (kk & 1) + 2 * t;
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][v], p.c, -mc));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][v + 1], p.c, -mc));
-        ls[t & 1] += e0 + e1;
-        w[t] = pack_bf16(e0, e1);
-      }
-      pf[kk] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-    }
-    l_sum += ls[0] + ls[1];
+    l_sum += ls;
   };
 
   if (n_steps > 0) {
