@@ -12,8 +12,10 @@ Prints one JSON line. `value` is effective TFLOP/s over retained pairs
 (4 * d * retained pairs per step / step time). Alongside, under "extra": the
 attention kernel alone (HIP events around each launch on the launch stream),
 the tile-map build, the same-shape dense run through the same kernel, the
-naive traversal (mask evaluated on every executed tile) and the tile-aligned
-variant; "cpu_baseline" times the float64 oracle on a bounded sample.
+naive traversal (mask evaluated on every executed tile), the tile-aligned
+variant, a tile-size search (svg_autotune_tiles) over {128, 256, 512} x {64,
+128, 256} and a plain bf16 GEMM for reference; "cpu_baseline" times the float64
+oracle on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
                     [--no-extras] [--cpu-rows 12288] [--profile] [--copy-calibration]
@@ -182,6 +184,30 @@ def cpu_baseline(w, Q, K, V, rows_per_head):
 
 # ------------------------------------------------------------------ roofline
 
+def gemm_reference(n=16384, reps=5):
+    """TFLOP/s of a plain bf16 GEMM (torch.matmul, the vendor BLAS) on N(0,1)
+    inputs: what the chip's MFMA pipes sustain on dense random data, at the
+    clock it holds under that load. Context for `roofline.frac`, which is
+    taken against the published peak at 2.4 GHz."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(11)
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    for _ in range(3):
+        c = a @ b
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return {"kind": f"torch.matmul bf16 {n}x{n}x{n}, N(0,1) inputs", "ms": round(ms, 4),
+            "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
+
+
 def measured_traffic():
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source; else None."""
@@ -249,6 +275,14 @@ def main():
         extra["tile_aligned_tflops_rounded_mask"] = round(
             4.0 * w.head_dim * tpairs / (np.mean(tattn) * 1e-3) / 1e12, 1)
         log(f"[bench] tile-aligned {np.mean(tattn):.3f} ms (pairs {tpairs / pairs - 1:+.3%})")
+        cands = [(bq, bk) for bq in (128, 256, 512) for bk in (64, 128, 256)]
+        best, cms = svg.svg_autotune_tiles(q, k, v, o, w.frames, w.grid_h, w.grid_w,
+                                           w.head_kinds, w.frame_window, w.band, cands,
+                                           sink_first_frame=w.sink, reps=3)
+        extra["tile_search_exact"] = {"candidates": cands, "ms": [round(x, 4) for x in cms],
+                                      "best": list(cands[best])}
+        log(f"[bench] tile search: best {cands[best]} at {cms[best]:.3f} ms "
+            f"({dict(zip(map(str, cands), [round(x, 3) for x in cms]))})")
         del q, k, v, o
         wd = si.workload("dense")
         (qd, kd, vd), _ = device_inputs(wd)
@@ -262,6 +296,10 @@ def main():
         log(f"[bench] dense {np.mean(dattn):.3f} ms -> sparse speed-up "
             f"{np.mean(dattn) / attn_ms:.2f}x")
         del qd, kd, vd, od
+        gref = gemm_reference()
+        gref["attn_achieved_over_gemm"] = round(achieved / gref["tflops"], 3)
+        extra["dense_gemm_reference"] = gref
+        log(f"[bench] reference GEMM {gref}")
     result = {
         "metric": METRIC,
         "value": round(value, 2),

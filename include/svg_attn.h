@@ -200,6 +200,28 @@ svg_status svg_attn_fwd(const void* q, const void* k, const void* v, void* o,
                         float scale, const int32_t* head_kind,
                         const svg_tile_map* map, uint32_t flags, void* stream);
 
+/* Tile-size search. The pages pick tile sizes by measured latency, not by
+ * the least boundary work ("Google Speeds Up Video Diffusion on TPUs with
+ * Optimized Sparse Attention", "Tile size tuning"; Newsbite, "Interesting
+ * facts" and "Actionable takeaways"). For each candidate i, (tile_q[i],
+ * tile_k[i]): build a tile map for `spec`, run svg_attn_fwd once untimed,
+ * then `reps` times between two HIP events on `stream`, and store the mean
+ * milliseconds per call in ms[i] (host array [n_cand]); *best receives the
+ * index of the smallest. q, k, v, o are as for svg_attn_fwd, with seq_len,
+ * num_heads and head kinds taken from `spec`; o is overwritten. scale as for
+ * svg_attn_fwd. Synchronous: returns after the last run has finished; maps
+ * are freed before it returns.
+ * Limits: 1 <= n_cand <= 256, 1 <= reps <= 1000.
+ * Errors: INVALID_ARG (null pointers, counts), UNSUPPORTED (a candidate or
+ * head_dim without a kernel; all candidates are checked before the first
+ * run), the errors of svg_build_tile_map and svg_attn_fwd, HIP. */
+svg_status svg_autotune_tiles(const svg_mask_spec* spec, const void* q,
+                              const void* k, const void* v, void* o,
+                              int32_t head_dim, float scale,
+                              const int32_t* tile_q, const int32_t* tile_k,
+                              int32_t n_cand, int32_t reps, void* stream,
+                              float* ms, int32_t* best);
+
 /* Token re-ordering between the original frame-major order t = f*S + s and
  * each head's kernel layout (temporal heads: p = s*F + f; other heads: p = t,
  * a plain copy). src, dst: device bf16 [num_heads][frames*tokens_per_frame]

@@ -8,6 +8,6 @@ from ._lib import (  # noqa: F401
     ERR_SHAPE_MISMATCH, ERR_UNSUPPORTED, EXPORTED, HEAD_DENSE, HEAD_SPATIAL,
     HEAD_TEMPORAL, LIB_PATH, OK, ROUND_EXACT, ROUND_TILE, TILE_BOUNDARY,
     TILE_FULL, TILE_SKIP, TO_KERNEL_LAYOUT, TO_ORIGINAL_LAYOUT, MaskSpec,
-    SvgError, TileMap, abi_version, load, svg_attn_fwd, svg_build_tile_map,
-    svg_permute_tokens,
+    SvgError, TileMap, abi_version, load, svg_attn_fwd, svg_autotune_tiles,
+    svg_build_tile_map, svg_permute_tokens,
 )

@@ -36,8 +36,8 @@ _KIND_NAMES = {"spatial": HEAD_SPATIAL, "temporal": HEAD_TEMPORAL, "dense": HEAD
 EXPORTED = (
     "svg_build_tile_map", "svg_tile_map_rebuild", "svg_tile_map_info_get",
     "svg_tile_map_stats", "svg_tile_map_copy_classes", "svg_tile_map_copy_schedule",
-    "svg_tile_map_destroy", "svg_attn_fwd", "svg_permute_tokens", "svg_last_error",
-    "svg_abi_version",
+    "svg_tile_map_destroy", "svg_attn_fwd", "svg_autotune_tiles", "svg_permute_tokens",
+    "svg_last_error", "svg_abi_version",
 )
 
 
@@ -95,6 +95,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "svg_tile_map_copy_schedule": (I32, [P, pI32, pI32, pI32, pI32, SZ]),
         "svg_tile_map_destroy": (I32, [P]),
         "svg_attn_fwd": (I32, [P, P, P, P, I64, I32, I32, ctypes.c_float, pI32, P, U32, P]),
+        "svg_autotune_tiles": (I32, [ctypes.POINTER(MaskSpec), P, P, P, P, I32, ctypes.c_float,
+                                     pI32, pI32, I32, I32, P, ctypes.POINTER(ctypes.c_float),
+                                     pI32]),
         "svg_permute_tokens": (I32, [P, P, I32, I32, I32, I32, pI32, I32, P]),
         "svg_last_error": (ctypes.c_char_p, []),
         "svg_abi_version": (I32, []),
@@ -222,6 +225,35 @@ def svg_attn_fwd(q, k, v, o, head_kind: Sequence[Union[str, int]], tile_map: Til
     _check(load().svg_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), N, H, d,
                                float(scale), _i32p(kinds), tile_map.handle, flags,
                                _stream(stream)))
+
+
+def svg_autotune_tiles(q, k, v, o, frames: int, grid_h: int, grid_w: int,
+                       head_kind: Sequence[Union[str, int]], frame_window: int,
+                       temporal_band: int, candidates: Sequence[tuple],
+                       sink_first_frame: bool = True, round_mode: int = ROUND_EXACT,
+                       reps: int = 3, scale: Optional[float] = None, stream=None):
+    """Time the attention forward for each (tile_q, tile_k) candidate.
+
+    Returns (index of the fastest candidate, list of mean ms per call)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _bf16_tensor(t, n)
+    H, N, d = q.shape
+    kinds = _kinds(head_kind)
+    if len(kinds) != H or N != frames * grid_h * grid_w:
+        raise ValueError("q's shape disagrees with the mask specification")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    spec = MaskSpec(frames, grid_h, grid_w, H, _i32p(kinds), frame_window, temporal_band,
+                    1 if sink_first_frame else 0, round_mode)
+    tq = np.ascontiguousarray([c[0] for c in candidates], dtype=np.int32)
+    tk = np.ascontiguousarray([c[1] for c in candidates], dtype=np.int32)
+    ms = (ctypes.c_float * max(1, len(candidates)))()
+    best = ctypes.c_int32(-1)
+    _check(load().svg_autotune_tiles(ctypes.byref(spec), q.data_ptr(), k.data_ptr(),
+                                     v.data_ptr(), o.data_ptr(), d, float(scale), _i32p(tq),
+                                     _i32p(tk), len(candidates), reps, _stream(stream), ms,
+                                     ctypes.byref(best)))
+    return int(best.value), [float(ms[i]) for i in range(len(candidates))]
 
 
 def svg_permute_tokens(src, dst, frames: int, tokens_per_frame: int,

@@ -346,4 +346,65 @@ svg_status svg_permute_tokens(const void* src, void* dst, int32_t frames,
   return ok();
 }
 
+svg_status svg_autotune_tiles(const svg_mask_spec* spec, const void* q, const void* k,
+                              const void* v, void* o, int32_t head_dim, float scale,
+                              const int32_t* tile_q, const int32_t* tile_k, int32_t n_cand,
+                              int32_t reps, void* stream, float* ms, int32_t* best) {
+  if (!spec || !spec->head_kind) return fail(SVG_ERR_INVALID_ARG, "spec or its head_kind is NULL");
+  if (!q || !k || !v || !o) return fail(SVG_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
+  if (!tile_q || !tile_k || !ms || !best)
+    return fail(SVG_ERR_INVALID_ARG, "tile_q, tile_k, ms and best must be non-NULL");
+  if (n_cand < 1 || n_cand > 256)
+    return fail(SVG_ERR_INVALID_ARG, "n_cand %d outside [1, 256]", n_cand);
+  if (reps < 1 || reps > 1000) return fail(SVG_ERR_INVALID_ARG, "reps %d outside [1, 1000]", reps);
+  for (int32_t i = 0; i < n_cand; ++i)
+    if (!tile_q_ok(tile_q[i]) || !tile_k_ok(tile_k[i]) ||
+        !svg::attn_supported(head_dim, tile_q[i], tile_k[i]))
+      return fail(SVG_ERR_UNSUPPORTED, "candidate %d: tiles %dx%d with head_dim %d have no kernel",
+                  i, tile_q[i], tile_k[i], head_dim);
+  const int64_t N = (int64_t)spec->frames * spec->grid_h * spec->grid_w;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  for (hipEvent_t& e : ev) {
+    const hipError_t he = hipEventCreate(&e);
+    if (he != hipSuccess) {
+      for (hipEvent_t x : ev)
+        if (x) (void)hipEventDestroy(x);
+      return hip_fail(he, "hipEventCreate");
+    }
+  }
+  svg_status status = SVG_OK;
+  int32_t arg = 0;
+  for (int32_t i = 0; i < n_cand && status == SVG_OK; ++i) {
+    svg_tile_map* map = nullptr;
+    status = svg_build_tile_map(spec, tile_q[i], tile_k[i], stream, &map);
+    if (status != SVG_OK) break;
+    auto run = [&]() {
+      return svg_attn_fwd(q, k, v, o, N, spec->num_heads, head_dim, scale, spec->head_kind, map,
+                          0, stream);
+    };
+    status = run();  // untimed: first touch of the map and the inputs
+    hipError_t he = hipSuccess;
+    if (status == SVG_OK) he = hipEventRecord(ev[0], st);
+    for (int32_t r = 0; r < reps && status == SVG_OK && he == hipSuccess; ++r) status = run();
+    if (status == SVG_OK && he == hipSuccess) he = hipEventRecord(ev[1], st);
+    if (status == SVG_OK && he == hipSuccess) he = hipEventSynchronize(ev[1]);
+    float t = 0.f;
+    if (status == SVG_OK && he == hipSuccess) he = hipEventElapsedTime(&t, ev[0], ev[1]);
+    if (status == SVG_OK && he != hipSuccess) status = hip_fail(he, "timing the attention runs");
+    if (status == SVG_OK) {
+      ms[i] = t / (float)reps;
+      if (ms[i] < ms[arg]) arg = i;
+    }
+    const std::string msg = g_last_error;
+    const svg_status ds = svg_tile_map_destroy(map);
+    if (status == SVG_OK) status = ds;
+    else g_last_error = msg;  // keep the first failure's message
+  }
+  for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  if (status != SVG_OK) return status;
+  *best = arg;
+  return ok();
+}
+
 }  // extern "C"

@@ -114,6 +114,30 @@ def test_attn_rejects_bad_arguments_before_hip(lib):
     assert "flags" in lib.svg_last_error().decode()
 
 
+def test_autotune_rejects_bad_arguments_before_hip(lib):
+    kinds = np.array([0, 1], dtype=np.int32)
+    kp = kinds.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    spec = _lib.MaskSpec(4, 8, 8, 2, kp, 1, 8, 1, 0)
+    p = 1 << 20  # never dereferenced: validation fails first
+    tq = np.array([256, 100], dtype=np.int32)
+    tk = np.array([128, 128], dtype=np.int32)
+    ip = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    ms = (ctypes.c_float * 2)()
+    best = ctypes.c_int32()
+    f = lib.svg_autotune_tiles
+    args = lambda **kw: dict(dict(spec=ctypes.byref(spec), q=p, k=p, v=p, o=p, d=64, sc=0.125,
+                                  tq=ip(tq), tk=ip(tk), n=1, reps=3, st=None, ms=ms,
+                                  best=ctypes.byref(best)), **kw).values()
+    assert f(*args(spec=None)) == svg.ERR_INVALID_ARG
+    assert f(*args(q=None)) == svg.ERR_INVALID_ARG
+    assert f(*args(n=0)) == svg.ERR_INVALID_ARG
+    assert f(*args(reps=0)) == svg.ERR_INVALID_ARG
+    assert f(*args(best=None)) == svg.ERR_INVALID_ARG
+    assert f(*args(n=2)) == svg.ERR_UNSUPPORTED        # tile_q 100 has no kernel
+    assert "candidate 1" in lib.svg_last_error().decode()
+    assert f(*args(d=96)) == svg.ERR_UNSUPPORTED       # head_dim 96 has no kernel
+
+
 def test_permute_rejects_bad_arguments_before_hip(lib):
     kinds = np.array([0, 1], dtype=np.int32)
     kp = kinds.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
