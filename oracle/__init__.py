@@ -21,6 +21,8 @@ What the pages fix, and where:
     (retained and dropped pairs mixed); full tiles take a mask-free path
     (marsel.app page, section "Efficient Kernel Implementation", tile-aware
     masking; Newsbite "Summary").
+  * Each head is routed to the spatial or the temporal mask from a sample of
+    its attention (same sections; routing.py gives the reading taken).
   * A tile-aligned variant rounds mask edges to the physical tiles so that few
     tiles need masking (StreamingMeme lead paragraph; Newsbite "Summary",
     "What changed").
@@ -38,6 +40,7 @@ from .masks import (DENSE, SPATIAL, TEMPORAL, MaskParams, HeadMask,
 from .tilemap import (SKIP, FULL, BOUNDARY, TileSchedule, tile_counts,
                       tile_classes, head_schedule, head_stats)
 from .attention import attention_rows, attention
+from .routing import Route, route_head, route_heads
 
 __all__ = [
     "DENSE", "SPATIAL", "TEMPORAL", "MaskParams", "HeadMask",
@@ -45,5 +48,5 @@ __all__ = [
     "to_kernel_layout", "to_original_layout",
     "SKIP", "FULL", "BOUNDARY", "TileSchedule", "tile_counts",
     "tile_classes", "head_schedule", "head_stats",
-    "attention_rows", "attention",
+    "attention_rows", "attention", "Route", "route_head", "route_heads",
 ]
