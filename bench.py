@@ -14,7 +14,8 @@ attention kernel alone (HIP events around each launch on the launch stream),
 the tile-map build, the same-shape dense run through the same kernel, the
 naive traversal (mask evaluated on every executed tile), the tile-aligned
 variant, a tile-size search (svg_autotune_tiles) over {128, 256, 512} x {64,
-128, 256} and a plain bf16 GEMM for reference; "cpu_baseline" times the float64
+128, 256}, sampled head routing (svg_route_heads; not part of the step, as on
+the pages) and a plain bf16 GEMM for reference; "cpu_baseline" times the float64
 oracle on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
@@ -182,6 +183,32 @@ def cpu_baseline(w, Q, K, V, rows_per_head):
                       f"{pairs} retained pairs, {cores} processes with single-threaded BLAS"}
 
 
+# ------------------------------------------------------------------ routing
+
+def routing_times(w, host):
+    """Wall time of svg_route_heads (synchronous: scratch allocation, V^T,
+    partial and combine kernels, copy-back) on the original-order inputs, at
+    64 sampled rows and at 1% of the tokens."""
+    import torch
+    import seeded_inputs as si
+    import structured_sparse_attention_amd as svg
+    q, k, v = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() for x in host)
+    out = {}
+    for n in (64, w.seq_len // 100):
+        rows = si.draw_query_subset(w, n, seed=77)
+        call = lambda: svg.svg_route_heads(q, k, v, w.frames, w.grid_h, w.grid_w,
+                                           w.frame_window, w.band, rows, sink_first_frame=w.sink)
+        call()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        kinds, err = call()
+        ms = (time.perf_counter() - t) * 1e3
+        out[f"rows_{n}"] = {"ms": round(ms, 3), "kinds": kinds}
+        log(f"[bench] routing {n} rows: {ms:.3f} ms, kinds {kinds}")
+    del q, k, v
+    return out
+
+
 # ------------------------------------------------------------------ roofline
 
 def gemm_reference(n=16384, reps=5):
@@ -275,6 +302,7 @@ def main():
         extra["tile_aligned_tflops_rounded_mask"] = round(
             4.0 * w.head_dim * tpairs / (np.mean(tattn) * 1e-3) / 1e12, 1)
         log(f"[bench] tile-aligned {np.mean(tattn):.3f} ms (pairs {tpairs / pairs - 1:+.3%})")
+        extra["routing"] = routing_times(w, host)
         cands = [(bq, bk) for bq in (128, 256, 512) for bk in (64, 128, 256)]
         best, cms = svg.svg_autotune_tiles(q, k, v, o, w.frames, w.grid_h, w.grid_w,
                                            w.head_kinds, w.frame_window, w.band, cands,

@@ -222,6 +222,35 @@ svg_status svg_autotune_tiles(const svg_mask_spec* spec, const void* q,
                               int32_t n_cand, int32_t reps, void* stream,
                               float* ms, int32_t* best);
 
+/* Sampled head routing ("Google Speeds Up Video Diffusion on TPUs with
+ * Optimized Sparse Attention", "Sparse Attention Patterns": each head is
+ * routed to the spatial or the temporal mask based on sampling). For every
+ * head and every sampled query row, attention is computed with every key,
+ * under the spatial mask and under the temporal mask (the masks of `spec`:
+ * frame_window, temporal_band, sink_first_frame). The error of a mask is the
+ * mean squared difference between its outputs and the dense ones over the
+ * sampled rows and the head_dim output columns; kinds[h] receives the mask
+ * with the smaller error (SVG_HEAD_SPATIAL on a tie).
+ *   spec:   frames, grid_h, grid_w, num_heads and the two windows are read;
+ *           head_kind and round_mode are ignored (head_kind may be NULL).
+ *   q, k, v: device bf16 [num_heads][N][head_dim], 16-byte aligned, in the
+ *           ORIGINAL frame-major order (routing precedes the layout step).
+ *   head_dim: 64 or 128; scale > 0 and finite (normally 1/sqrt(head_dim)).
+ *   rows:   host int32 [n_rows], original-order query indices in [0, N),
+ *           drawn by the caller; 1 <= n_rows <= 65536; repeats allowed.
+ *   err:    host float [num_heads][2] (spatial, temporal error), or NULL.
+ *   kinds:  host int32 [num_heads].
+ * The scores use bf16 inputs and fp32 accumulation; P is rounded to bf16
+ * for the PV product, as in svg_attn_fwd. Allocates a device scratch of
+ * about num_heads*N*head_dim*2 + num_heads*n_rows*(N/32 splits at most)*...
+ * bytes (V^T plus per-split partial results), freed before return.
+ * Synchronous: returns after the results are on the host.
+ * Errors: INVALID_ARG, UNSUPPORTED (head_dim), ALIGNMENT, OOM, HIP. */
+svg_status svg_route_heads(const svg_mask_spec* spec, const void* q,
+                           const void* k, const void* v, int32_t head_dim,
+                           float scale, const int32_t* rows, int32_t n_rows,
+                           void* stream, float* err, int32_t* kinds);
+
 /* Token re-ordering between the original frame-major order t = f*S + s and
  * each head's kernel layout (temporal heads: p = s*F + f; other heads: p = t,
  * a plain copy). src, dst: device bf16 [num_heads][frames*tokens_per_frame]

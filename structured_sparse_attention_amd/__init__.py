@@ -9,5 +9,5 @@ from ._lib import (  # noqa: F401
     HEAD_TEMPORAL, LIB_PATH, OK, ROUND_EXACT, ROUND_TILE, TILE_BOUNDARY,
     TILE_FULL, TILE_SKIP, TO_KERNEL_LAYOUT, TO_ORIGINAL_LAYOUT, MaskSpec,
     SvgError, TileMap, abi_version, load, svg_attn_fwd, svg_autotune_tiles,
-    svg_build_tile_map, svg_permute_tokens,
+    svg_build_tile_map, svg_permute_tokens, svg_route_heads,
 )

@@ -36,8 +36,8 @@ _KIND_NAMES = {"spatial": HEAD_SPATIAL, "temporal": HEAD_TEMPORAL, "dense": HEAD
 EXPORTED = (
     "svg_build_tile_map", "svg_tile_map_rebuild", "svg_tile_map_info_get",
     "svg_tile_map_stats", "svg_tile_map_copy_classes", "svg_tile_map_copy_schedule",
-    "svg_tile_map_destroy", "svg_attn_fwd", "svg_autotune_tiles", "svg_permute_tokens",
-    "svg_last_error", "svg_abi_version",
+    "svg_tile_map_destroy", "svg_attn_fwd", "svg_autotune_tiles", "svg_route_heads",
+    "svg_permute_tokens", "svg_last_error", "svg_abi_version",
 )
 
 
@@ -98,6 +98,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "svg_autotune_tiles": (I32, [ctypes.POINTER(MaskSpec), P, P, P, P, I32, ctypes.c_float,
                                      pI32, pI32, I32, I32, P, ctypes.POINTER(ctypes.c_float),
                                      pI32]),
+        "svg_route_heads": (I32, [ctypes.POINTER(MaskSpec), P, P, P, I32, ctypes.c_float, pI32,
+                                  I32, P, ctypes.POINTER(ctypes.c_float), pI32]),
         "svg_permute_tokens": (I32, [P, P, I32, I32, I32, I32, pI32, I32, P]),
         "svg_last_error": (ctypes.c_char_p, []),
         "svg_abi_version": (I32, []),
@@ -254,6 +256,37 @@ def svg_autotune_tiles(q, k, v, o, frames: int, grid_h: int, grid_w: int,
                                      _i32p(tk), len(candidates), reps, _stream(stream), ms,
                                      ctypes.byref(best)))
     return int(best.value), [float(ms[i]) for i in range(len(candidates))]
+
+
+def svg_route_heads(q, k, v, frames: int, grid_h: int, grid_w: int, frame_window: int,
+                    temporal_band: int, rows, sink_first_frame: bool = True,
+                    scale: Optional[float] = None, stream=None):
+    """Route each head to the spatial or temporal mask from sampled query rows.
+
+    q, k, v: bf16 [H, N, d] in the original frame-major order; rows: original
+    query indices. Returns (kinds: list of "spatial"/"temporal", err: float32
+    [H, 2] numpy array of the spatial and temporal mean squared errors)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _bf16_tensor(t, n)
+    H, N, d = q.shape
+    for t, n in ((k, "k"), (v, "v")):
+        if tuple(t.shape) != (H, N, d):
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {(H, N, d)}")
+    if N != frames * grid_h * grid_w:
+        raise ValueError("q's shape disagrees with frames * grid_h * grid_w")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    r = np.ascontiguousarray(rows, dtype=np.int32)
+    spec = MaskSpec(frames, grid_h, grid_w, H, None, frame_window, temporal_band,
+                    1 if sink_first_frame else 0, ROUND_EXACT)
+    err = np.zeros((H, 2), dtype=np.float32)
+    kinds = np.zeros(H, dtype=np.int32)
+    _check(load().svg_route_heads(ctypes.byref(spec), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  d, float(scale), _i32p(r), len(r), _stream(stream),
+                                  err.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                  _i32p(kinds)))
+    names = {HEAD_SPATIAL: "spatial", HEAD_TEMPORAL: "temporal"}
+    return [names[int(x)] for x in kinds], err
 
 
 def svg_permute_tokens(src, dst, frames: int, tokens_per_frame: int,

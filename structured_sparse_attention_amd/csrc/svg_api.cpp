@@ -407,4 +407,61 @@ svg_status svg_autotune_tiles(const svg_mask_spec* spec, const void* q, const vo
   return ok();
 }
 
+svg_status svg_route_heads(const svg_mask_spec* spec, const void* q, const void* k, const void* v,
+                           int32_t head_dim, float scale, const int32_t* rows, int32_t n_rows,
+                           void* stream, float* err, int32_t* kinds) {
+  if (!spec) return fail(SVG_ERR_INVALID_ARG, "spec is NULL");
+  if (!q || !k || !v) return fail(SVG_ERR_INVALID_ARG, "q, k and v must be non-NULL");
+  if (!rows || !kinds) return fail(SVG_ERR_INVALID_ARG, "rows and kinds must be non-NULL");
+  if (spec->frames < 1 || spec->grid_h < 1 || spec->grid_w < 1)
+    return fail(SVG_ERR_INVALID_ARG, "frames, grid_h and grid_w must be >= 1");
+  const int64_t S = (int64_t)spec->grid_h * spec->grid_w;
+  const int64_t N = S * spec->frames;
+  if (S > (1 << 30) || N > (1 << 30))
+    return fail(SVG_ERR_INVALID_ARG, "sequence of %lld tokens exceeds 2^30", (long long)N);
+  if (spec->num_heads < 1 || spec->num_heads > 4096)
+    return fail(SVG_ERR_INVALID_ARG, "num_heads %d outside [1, 4096]", spec->num_heads);
+  if (spec->frame_window < 0 || spec->temporal_band < 0)
+    return fail(SVG_ERR_INVALID_ARG, "frame_window and temporal_band must be >= 0");
+  if (n_rows < 1 || n_rows > 65536)
+    return fail(SVG_ERR_INVALID_ARG, "n_rows %d outside [1, 65536]", n_rows);
+  for (int32_t i = 0; i < n_rows; ++i)
+    if (rows[i] < 0 || rows[i] >= N)
+      return fail(SVG_ERR_INVALID_ARG, "rows[%d] = %d outside [0, %lld)", i, rows[i],
+                  (long long)N);
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(SVG_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SVG_ERR_UNSUPPORTED, "head_dim %d: supported are 64 and 128", head_dim);
+  if (N * head_dim * 2 >= ((int64_t)1 << 31))
+    return fail(SVG_ERR_UNSUPPORTED, "one head of %lld x %d bf16 values exceeds 2 GiB",
+                (long long)N, head_dim);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(SVG_ERR_ALIGNMENT, "q, k and v must be 16-byte aligned");
+  const int32_t H = spec->num_heads;
+  const svg::RouteLayout L = svg::route_layout(N, H, head_dim, n_rows);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* scratch = nullptr;
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&scratch), (size_t)L.bytes);
+  if (e != hipSuccess) return fail(SVG_ERR_OOM, "routing scratch of %lld bytes: %s",
+                                   (long long)L.bytes, hipGetErrorString(e));
+  std::vector<float> err_h((size_t)H * 2);
+  e = hipMemcpyAsync(scratch + L.rows_off, rows, (size_t)n_rows * 4, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess)
+    e = svg::launch_route(q, k, v, scratch, L, N, spec->frames, (int32_t)S, H, head_dim,
+                          spec->frame_window, spec->temporal_band, spec->sink_first_frame ? 1 : 0,
+                          scale, n_rows, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(err_h.data(), scratch + L.err_off, err_h.size() * 4,
+                       hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(kinds, scratch + L.kind_off, (size_t)H * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  const hipError_t fe = hipFree(scratch);
+  if (e != hipSuccess) return hip_fail(e, "routing kernels");
+  if (fe != hipSuccess) return hip_fail(fe, "hipFree");
+  if (err) std::memcpy(err, err_h.data(), err_h.size() * 4);
+  return ok();
+}
+
 }  // extern "C"

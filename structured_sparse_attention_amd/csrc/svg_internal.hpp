@@ -55,6 +55,21 @@ hipError_t launch_attn_fwd(const MapGeometry& g, const MapBuffers& b,
                            const AttnArgs& a, hipStream_t stream);
 bool attn_supported(int32_t head_dim, int32_t tile_q, int32_t tile_k);
 
+// Scratch of one routing call (byte offsets into one allocation).
+struct RouteLayout {
+  int64_t pitch;      // columns per V^T row
+  int64_t split_len;  // keys per split (a multiple of 32)
+  int64_t n_split;
+  int64_t vt_off, rows_off, part_off, row_err_off, err_off, kind_off, bytes;
+};
+RouteLayout route_layout(int64_t N, int32_t H, int32_t D, int32_t n_rows);
+// Queue the routing kernels; the sampled rows must already be at
+// scratch + rows_off. Results: float [H][2] at err_off, int32 [H] at kind_off.
+hipError_t launch_route(const void* q, const void* k, const void* v, char* scratch,
+                        const RouteLayout& L, int64_t N, int32_t F, int32_t S, int32_t H,
+                        int32_t D, int32_t W_f, int32_t W_s, int32_t sink, float scale,
+                        int32_t n_rows, hipStream_t stream);
+
 // kinds: host array [H]; one launch per head.
 hipError_t launch_permute_tokens(const void* src, void* dst, int32_t F,
                                  int32_t S, int32_t H, int32_t D,

@@ -138,6 +138,30 @@ def test_autotune_rejects_bad_arguments_before_hip(lib):
     assert f(*args(d=96)) == svg.ERR_UNSUPPORTED       # head_dim 96 has no kernel
 
 
+def test_route_rejects_bad_arguments_before_hip(lib):
+    spec = _lib.MaskSpec(4, 8, 8, 2, None, 1, 8, 1, 0)
+    p = 1 << 20  # never dereferenced: validation fails first
+    rows = np.array([0, 5, 255], dtype=np.int32)
+    bad = np.array([0, 256], dtype=np.int32)
+    ip = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    kinds = np.zeros(2, dtype=np.int32)
+    f = lib.svg_route_heads
+    assert f(None, p, p, p, 64, 0.125, ip(rows), 3, None, None, ip(kinds)) == svg.ERR_INVALID_ARG
+    assert f(ctypes.byref(spec), None, p, p, 64, 0.125, ip(rows), 3, None, None,
+             ip(kinds)) == svg.ERR_INVALID_ARG
+    assert f(ctypes.byref(spec), p, p, p, 64, 0.125, ip(bad), 2, None, None,
+             ip(kinds)) == svg.ERR_INVALID_ARG
+    assert "rows[1]" in lib.svg_last_error().decode()
+    assert f(ctypes.byref(spec), p, p, p, 64, 0.125, ip(rows), 0, None, None,
+             ip(kinds)) == svg.ERR_INVALID_ARG
+    assert f(ctypes.byref(spec), p, p, p, 64, -1.0, ip(rows), 3, None, None,
+             ip(kinds)) == svg.ERR_INVALID_ARG
+    assert f(ctypes.byref(spec), p, p, p, 96, 0.125, ip(rows), 3, None, None,
+             ip(kinds)) == svg.ERR_UNSUPPORTED
+    assert f(ctypes.byref(spec), p + 8, p, p, 64, 0.125, ip(rows), 3, None, None,
+             ip(kinds)) == svg.ERR_ALIGNMENT
+
+
 def test_permute_rejects_bad_arguments_before_hip(lib):
     kinds = np.array([0, 1], dtype=np.int32)
     kp = kinds.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
