@@ -223,8 +223,8 @@ svg_status svg_autotune_tiles(const svg_mask_spec* spec, const void* q,
                               float* ms, int32_t* best);
 
 /* Sampled head routing ("Google Speeds Up Video Diffusion on TPUs with
- * Optimized Sparse Attention", "Sparse Attention Patterns": each head is
- * routed to the spatial or the temporal mask based on sampling). For every
+ * Optimized Sparse Attention", "Sparse Attention Patterns": the mask of each
+ * head, spatial or temporal, is chosen from a sample). For every
  * head and every sampled query row, attention is computed with every key,
  * under the spatial mask and under the temporal mask (the masks of `spec`:
  * frame_window, temporal_band, sink_first_frame). The error of a mask is the
@@ -241,9 +241,10 @@ svg_status svg_autotune_tiles(const svg_mask_spec* spec, const void* q,
  *   err:    host float [num_heads][2] (spatial, temporal error), or NULL.
  *   kinds:  host int32 [num_heads].
  * The scores use bf16 inputs and fp32 accumulation; P is rounded to bf16
- * for the PV product, as in svg_attn_fwd. Allocates a device scratch of
- * about num_heads*N*head_dim*2 + num_heads*n_rows*(N/32 splits at most)*...
- * bytes (V^T plus per-split partial results), freed before return.
+ * for the PV product, as in svg_attn_fwd. Allocates one device scratch
+ * (V^T of every head, num_heads*head_dim*(N+128)*2 bytes at most, plus
+ * per-split partial results of about 1.6 KB per sampled row, head and
+ * split), freed before return.
  * Synchronous: returns after the results are on the host.
  * Errors: INVALID_ARG, UNSUPPORTED (head_dim), ALIGNMENT, OOM, HIP. */
 svg_status svg_route_heads(const svg_mask_spec* spec, const void* q,
