@@ -20,6 +20,7 @@ oracle on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
                     [--no-extras] [--cpu-rows 12288] [--profile] [--copy-calibration]
+                    [--routing-only]
 """
 from __future__ import annotations
 
@@ -61,6 +62,8 @@ def parse():
                     help="few steps, main workload only (for rocprofv3)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--routing-only", action="store_true",
+                    help="run only the sampled head routing on the main workload")
     return ap.parse_args()
 
 
@@ -258,6 +261,11 @@ def main():
         sys.exit(2)
     if a.copy_calibration:
         return copy_calibration()
+    if a.routing_only:
+        import seeded_inputs as si
+        w = si.workload("main")
+        print(json.dumps({"routing": routing_times(w, si.draw_qkv(w))}), flush=True)
+        return
     import torch
     import seeded_inputs as si
     if a.profile:
