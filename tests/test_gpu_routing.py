@@ -70,7 +70,12 @@ CASES = [si.workload("tiny"), si.workload("tiny-misaligned"), RAGGED, RAGGED_NOS
          si.Workload("short-frames", 9, 3, 5, ("spatial", "temporal"), 64, 1, 2, True, 32, 32,
                      False, seed=42),
          si.Workload("short-frames-nosink", 9, 3, 5, ("spatial", "temporal"), 128, 2, 1, False,
-                     32, 32, False, seed=43)]
+                     32, 32, False, seed=43),
+         # one token; one token per frame (every step spans 32 frames)
+         si.Workload("one-token", 1, 1, 1, ("spatial", "temporal"), 64, 0, 0, True, 32, 32,
+                     False, seed=44),
+         si.Workload("token-frames", 70, 1, 1, ("spatial", "temporal"), 128, 3, 0, True, 32, 32,
+                     False, seed=45)]
 
 
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
