@@ -37,10 +37,13 @@
 // rows are padded (272 bytes, and 144 for V^T) so that 16 lanes reading 16
 // consecutive rows at one column hit 16 distinct 4-bank groups of the 64
 // banks. K rows are stored in the order the S^T accumulator layout needs for
-// P^T to be the B operand of the PV product as it stands. Workgroups are
-// remapped so that consecutive Q tiles of a head run on the same XCD and
-// share its L2, in blocks dealt out in rounds so that the XCDs stay
-// balanced.
+// P^T to be the B operand of the PV product as it stands; V rows in an order
+// that keeps the transposing reads free of bank conflicts. A step's first
+// row is folded into the base of its buffer resources, so the loads need no
+// per-lane address arithmetic and rows past the sequence read as zeros.
+// Workgroups are remapped so that consecutive Q tiles of a head run on the
+// same XCD and share its L2, in blocks dealt out in rounds so that the XCDs
+// stay balanced.
 #include "svg_internal.hpp"
 
 #include <math.h>
@@ -119,6 +122,15 @@ __device__ __forceinline__ int sigma(int m) {
   return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
 }
 
+// V rows are stored in another order: LDS row m holds key vkey(m), so that
+// the four keys 4b..4b+3 of a 16-key block sit 4 rows apart. A transposing
+// read of 4 keys x 64 dims then spans rows 4 x 272 bytes apart, 16 banks
+// apart, and its 32 lanes of 8 bytes hit 64 distinct banks (with
+// consecutive rows they would hit the same banks 2 to 4 times).
+__device__ __forceinline__ int vkey(int m) {
+  return (m & ~15) | ((m & 3) << 2) | ((m >> 2) & 3);
+}
+
 // Logical workgroup of launch index i (T workgroups). The hardware deals
 // launch indices round-robin over the 8 XCDs; XCD x then takes blocks of XB
 // consecutive logical workgroups (consecutive Q tiles of a head, which share
@@ -167,21 +179,17 @@ __device__ __forceinline__ Step make_step(const KParams& p, int ti, int bnd, int
   return s;
 }
 
-// Row of key r (0..63) of a step, clamped into the sequence (keys past
-// `ncols` are masked; their row only has to be readable).
-__device__ __forceinline__ int key_row(const KParams& p, const Step& s, int r) {
-  return min(s.base + (r < s.ncols ? r : 0) * s.stride, p.N - 1);
-}
-
 // Staging of one step. K rows and V rows move from HBM straight into LDS
-// (buffer_load ... lds, no VGPRs), both in the same padded row layout and
-// row order (LDS row m of a 32-row block holds key sigma(m)). The (row,
-// chunk) a lane fetches in load j is fixed; its byte offset is computed per
-// step from the step's first row, row stride and column count, with rows
-// past the count clamped to the step's first row (they are masked) and
-// every row clamped into the sequence, so one branch-free sequence serves
-// full, strided (sink) and short steps. Pad slots re-read chunk 0 of their
-// row (in bounds, never read back).
+// (buffer_load ... lds, no VGPRs), both in the same padded row layout (LDS
+// row m of a 32-row K block holds key sigma(m); LDS row m of V holds key
+// vkey(m)). The (row,
+// chunk) a lane fetches in load j is fixed, so its byte offset from the
+// step's first row is too: one table for steps of consecutive rows, one for
+// sink steps at a stride of F rows. The step's first row goes into the base
+// of the buffer resources, whose record count ends at the end of the
+// sequence: rows past it read as zeros (the buffer range check), rows past
+// the step's column count are masked, and a load costs no address
+// arithmetic. Pad slots re-read chunk 0 of their row (never read back).
 //
 // V is then transposed inside LDS once per step: each 16-lane group reads 4
 // keys x 16 dims with one ds_read_b64_tr_b16 (lane j gets dim j of the 4
@@ -191,17 +199,40 @@ template <int D, int NW>
 struct Stage {
   using Lt = Layout<D, NW>;
   static constexpr int ROWB = 2 * D;  // bytes per K/V row in HBM
-  static constexpr int SH = D == 128 ? 8 : 7;
-  uint32_t koff[Lt::LPW];  // row-in-step << SH | byte in row, per load
+  // Byte offsets from the step's first row, per load: K and V rows, for
+  // consecutive rows and at a row stride of F (saturated: past the end).
+  uint32_t koff[Lt::LPW], koffs[Lt::LPW], voff[Lt::LPW], voffs[Lt::LPW];
 
-  __device__ __forceinline__ void init(int wl, int lane) {
+  __device__ __forceinline__ void init(int wl, int lane, int F) {
+    auto put = [&](int r, uint32_t byte, uint32_t& o, uint32_t& os) {
+      o = (uint32_t)(r * ROWB) + byte;
+      const uint64_t fs = (uint64_t)r * (uint64_t)F * ROWB + byte;
+      os = fs < 0x80000000ull ? (uint32_t)fs : 0x80000000u;
+    };
 #pragma unroll
     for (int i = 0; i < Lt::LPW; ++i) {
-      const int slot = (i * Lt::NL + wl) * 64 + lane;
+      // a wave with no load i repeats its load i-1
+      const int si = i == 0 || k_ok(i, wl) ? i : i - 1;
+      const int slot = (si * Lt::NL + wl) * 64 + lane;
       const int prow = slot / Lt::KSLOTS, c = slot - prow * Lt::KSLOTS;
-      const int r = (prow & ~31) | sigma(prow & 31);
-      koff[i] = (uint32_t)(r * ROWB + 16 * (c < Lt::NCH ? c : 0));
+      const uint32_t byte = 16 * (c < Lt::NCH ? c : 0);
+      put((prow & ~31) | sigma(prow & 31), byte, koff[i], koffs[i]);
+      put(vkey(prow), byte, voff[i], voffs[i]);
     }
+  }
+
+  // Buffer resources of a step: K and V of the head from the step's first
+  // row (clamped to the end of the sequence) to the end of the sequence.
+  struct Src {
+    __amdgpu_buffer_rsrc_t k, v;
+  };
+  __device__ __forceinline__ static Src src(const KParams& p, const uint16_t* kh,
+                                            const uint16_t* vh, const Step& s) {
+    const int b = min(s.base, p.N);
+    const int n = (p.N - b) * ROWB;
+    const size_t e = (size_t)b * D;
+    return {__builtin_amdgcn_make_buffer_rsrc((void*)(kh + e), (short)0, n, 0x00020000),
+            __builtin_amdgcn_make_buffer_rsrc((void*)(vh + e), (short)0, n, 0x00020000)};
   }
 
   __device__ __forceinline__ bool k_ok(int i, int wl) const {
@@ -211,19 +242,19 @@ struct Stage {
   // Load pair j (K and V rows of one 1 KiB slot) of step `s` into `buf`,
   // without a branch: a wave that has no load j repeats its load j-1 (the
   // same bytes to the same place).
-  __device__ __forceinline__ void load(const KParams& p, __amdgpu_buffer_rsrc_t krs,
-                                       __amdgpu_buffer_rsrc_t vrs, const Step& s, char* buf,
-                                       int wl, int j) const {
+  __device__ __forceinline__ void load(const Src& sr, const Step& s, char* buf, int wl,
+                                       int j) const {
+    // (the tables already hold the repeated load; indices stay compile-time
+    // constants, which keeps the tables in registers)
     const bool ok = j == 0 || k_ok(j, wl);
     const int jj = ok ? j : j - 1;
-    const uint32_t ko = koff[j > 0 && !ok ? j - 1 : j];
-    const int r = (int)(ko >> SH);
-    const int row = min(s.base + (r < s.ncols ? r : 0) * s.stride, p.N - 1);
-    const uint32_t off = (uint32_t)row * ROWB + (ko & (ROWB - 1));
+    const bool one = s.stride == 1;
+    const uint32_t ko = one ? koff[j] : koffs[j];
+    const uint32_t vo = one ? voff[j] : voffs[j];
     const int at = (jj * Lt::NL + wl) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(buf + at), 16, off, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(buf + Lt::VR_OFF + at), 16, off, 0,
-                                             0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr.k, (lds_void*)(buf + at), 16, ko, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr.v, (lds_void*)(buf + Lt::VR_OFF + at), 16, vo,
+                                             0, 0, 0);
   }
 
   // V rows of `src` -> V^T of `dst` (this transposer wave's share). Chunk
@@ -235,13 +266,13 @@ struct Stage {
   };
   __device__ __forceinline__ static TrLane tr_lane(int lane) {
     const int q = lane >> 4, jj = lane & 15;
-    return {(jj >> 2) * Lt::KROW + 2 * (16 * q + 4 * (jj & 3)), (16 * q + jj) * Lt::VTROW};
+    return {(jj >> 2) * 4 * Lt::KROW + 2 * (16 * q + 4 * (jj & 3)), (16 * q + jj) * Lt::VTROW};
   }
   // uniform part of pass t: read offsets of keys 8g..8g+3 and 8g+4..8g+7
-  // (LDS rows sigma(key): sigma is its own inverse) and the write offset
+  // (key 16a + 4b + i sits in V row 16a + 4i + b) and the write offset
   __device__ __forceinline__ static int tr_rd(int wt, int t, int half) {
     const int u = t * Lt::NT + wt, dd = (u % (D / 64)) * 64, g = u / (D / 64);
-    const int pr = 32 * (g >> 2) + sigma(8 * (g & 3) + 4 * half);
+    const int pr = 16 * (g >> 1) + 2 * (g & 1) + half;
     return Lt::VR_OFF + pr * Lt::KROW + 2 * dd;
   }
   __device__ __forceinline__ static int tr_wr(int wt, int t) {
@@ -378,11 +409,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
 
   const size_t head_off = (size_t)h * p.N * D;
   const uint16_t* Qh = p.q + head_off;
-  const int head_bytes = p.N * D * 2;
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + head_off), (short)0, head_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + head_off), (short)0, head_bytes, 0x00020000);
+  const uint16_t* Kh = p.k + head_off;
+  const uint16_t* Vh = p.v + head_off;
 
   // Group 0 (every wave with fewer than eight) issues the HBM loads, group 1
   // (every wave with fewer than eight) transposes V.
@@ -390,7 +418,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
   const int wl = wave, wt = PP ? wave - NW / 2 : wave;
   const typename Stage<D, NW>::TrLane tl = Stage<D, NW>::tr_lane(lane);
   Stage<D, NW> stg;
-  if (loader) stg.init(wl, lane);
+  if (loader) stg.init(wl, lane, p.F);
   // Stage 0 holds the first step's K and V rows; its V^T area holds zeros,
   // which the first MFMA phase multiplies by P = 0.
   Cursor cur_pos;
@@ -400,7 +428,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
     st_t = cur_pos.next(p);
     if (loader)
 #pragma unroll
-      for (int j = 0; j < Lt::LPW; ++j) stg.load(p, krs, vrs, st_t, buf0, wl, j);
+      for (int j = 0; j < Lt::LPW; ++j)
+        stg.load(Stage<D, NW>::src(p, Kh, Vh, st_t), st_t, buf0, wl, j);
   }
   for (int off = threadIdx.x * 16; off < Lt::VTILE; off += NW * 64 * 16)
     *(uint4*)(buf0 + Lt::VT_OFF + off) = make_uint4(0, 0, 0, 0);
@@ -639,14 +668,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
           // few). After the last step they fetch rows of the last step again
           // into a stage nobody reads.
           struct DmaSide {
-            const KParams& p;
             const Stage<D, NW>& stg;
-            __amdgpu_buffer_rsrc_t krs, vrs;
+            typename Stage<D, NW>::Src sr;
             const Step& st;
             char* nb;
             int wl;
             __device__ __forceinline__ void at(int i) const {
-              if (i % LS == 0 && i / LS < Lt::LPW) stg.load(p, krs, vrs, st, nb, wl, i / LS);
+              if (i % LS == 0 && i / LS < Lt::LPW) stg.load(sr, st, nb, wl, i / LS);
             }
             __device__ __forceinline__ void pattern(int i) const {
               if (i % LS == 0 && i / LS < Lt::LPW) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
@@ -655,7 +683,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
           static_assert(Lt::LPW <= NM, "every load pair needs an MFMA slot");
           if (!PP) Stage<D, NW>::transpose(cb, nb, tl, wt);
           st_nn = cur_pos.next(p);
-          mphase(cb, DmaSide{p, stg, krs, vrs, st_next, nb, wl});
+          mphase(cb, DmaSide{stg, Stage<D, NW>::src(p, Kh, Vh, st_next), st_next, nb, wl});
           if (PP) phase_barrier();
           if (has_v) vphase(st_t);
         } else {
