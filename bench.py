@@ -13,7 +13,7 @@ Prints one JSON line. `value` is effective TFLOP/s over retained pairs
 attention kernel alone (HIP events around each launch on the launch stream),
 the tile-map build, the same-shape dense run through the same kernel, the
 naive traversal (mask evaluated on every executed tile), the tile-aligned
-variant, a tile-size search (svg_autotune_tiles) over {128, 256, 512} x {64,
+variant, the 1440p workload (302,400 tokens), a tile-size search (svg_autotune_tiles) over {128, 256, 512} x {64,
 128, 256}, sampled head routing (svg_route_heads; not part of the step, as on
 the pages) and a plain bf16 GEMM for reference; "cpu_baseline" times the float64
 oracle on a bounded sample.
@@ -332,6 +332,18 @@ def main():
         log(f"[bench] dense {np.mean(dattn):.3f} ms -> sparse speed-up "
             f"{np.mean(dattn) / attn_ms:.2f}x")
         del qd, kd, vd, od
+        wl = si.workload("1440p")
+        (ql, kl, vl), _ = device_inputs(wl)
+        ol = torch.empty_like(ql)
+        _, lattn, lmap, lstats = time_steps(wl, ql, kl, vl, ol, 3, 1)
+        lpairs = sum(s["retained_pairs"] for s in lstats)
+        extra["1440p_attn_kernel_ms"] = round(float(np.mean(lattn)), 3)
+        extra["1440p_tile_map_ms"] = round(float(np.mean(lmap)), 4)
+        extra["1440p_tflops"] = round(4.0 * wl.head_dim * lpairs
+                                      / (np.mean(lattn) * 1e-3) / 1e12, 1)
+        log(f"[bench] 1440p (N={wl.seq_len}) {np.mean(lattn):.3f} ms, "
+            f"{extra['1440p_tflops']} effective TFLOP/s")
+        del ql, kl, vl, ol
         gref = gemm_reference()
         gref["attn_achieved_over_gemm"] = round(achieved / gref["tflops"], 3)
         extra["dense_gemm_reference"] = gref
