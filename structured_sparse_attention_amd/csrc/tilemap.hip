@@ -25,39 +25,42 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ int64_t span(int64_t a, int64_t b) { return b > a ? b - a : 0; }
 __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-// multiples of F in [a, b), a >= 0
-__device__ __forceinline__ int64_t multiples(int64_t a, int64_t b, int64_t F) {
-  return b > a ? cdiv(b, F) - cdiv(a, F) : 0;
-}
+
+// 32-bit counting: sequences are at most 2^30 tokens and a tile holds at most
+// 512 x 1024 pairs, so every per-tile quantity fits; only the sums over a
+// row of tiles need 64 bits.
+__device__ __forceinline__ int span32(int a, int b) { return b > a ? b - a : 0; }
+// min(lim, v + w + 1) without forming v + w + 1 (w may be near INT32_MAX)
+__device__ __forceinline__ int upper(int v, int w, int lim) { return w >= lim - v ? lim : v + w + 1; }
 
 struct Counts {
-  int64_t mask;     // retained pairs of the exact mask
-  int64_t contig;   // pairs of the contiguous part (spatial: all; temporal: band)
+  int mask;    // retained pairs of the exact mask
+  int contig;  // pairs of the contiguous part (spatial: all; temporal: band)
 };
 
-// Retained columns in [c0, c1) of one row whose run coordinate is v.
-__device__ __forceinline__ Counts row_columns(const MapGeometry& g, int kind,
-                                              int64_t v, int64_t c0, int64_t c1) {
+// Retained columns in [c0, c1) of one row whose run coordinate is v. For
+// temporal heads C0 = ceil(c0 / F) and C1 = ceil(c1 / F) bound the sink
+// columns (multiples of F) of the tile; the band ends are multiples of F,
+// so the sink columns inside the band need no division.
+__device__ __forceinline__ Counts row_columns(const MapGeometry& g, int kind, int v, int c0,
+                                              int c1, int C0, int C1) {
   Counts r;
   if (kind == SVG_HEAD_SPATIAL) {
-    const int64_t lo = max<int64_t>(0, v - g.W_f) * g.S;
-    const int64_t hi = min<int64_t>(g.F, v + g.W_f + 1) * g.S;
-    int64_t n = span(max(lo, c0), min(hi, c1));
+    const int lo = max(0, v - g.W_f) * g.S;
+    const int hi = upper(v, g.W_f, g.F) * g.S;
+    int n = span32(max(lo, c0), min(hi, c1));
     if (g.sink) {
-      n += span(c0, min<int64_t>(g.S, c1));
-      n -= span(max(lo, c0), min(min<int64_t>(hi, g.S), c1));
+      n += span32(c0, min(g.S, c1));
+      n -= span32(max(lo, c0), min(min(hi, g.S), c1));
     }
     r.mask = n;
     r.contig = n;
   } else {  // temporal
-    const int64_t lo = max<int64_t>(0, v - g.W_s) * g.F;
-    const int64_t hi = min<int64_t>(g.S, v + g.W_s + 1) * g.F;
-    const int64_t a = max(lo, c0), b = min(hi, c1);
-    const int64_t band = span(a, b);
+    const int lo_s = max(0, v - g.W_s), hi_s = upper(v, g.W_s, g.S);
+    const int band = span32(max(lo_s * g.F, c0), min(hi_s * g.F, c1));
     r.contig = band;
-    r.mask = band + (g.sink ? multiples(c0, c1, g.F) - multiples(a, max(a, b), g.F) : 0);
+    r.mask = band + (g.sink ? (C1 - C0) - span32(max(lo_s, C0), min(hi_s, C1)) : 0);
   }
   return r;
 }
@@ -106,17 +109,20 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MapGeometry g, MapBu
   // skip, full, boundary, exec_full, exec_boundary, retained
   int64_t acc[6] = {0, 0, 0, 0, 0, 0};
   uint8_t* cls_row = b.classes + row * g.nK;
-  for (int64_t kt = threadIdx.x; kt < g.nK; kt += kThreads) {
-    const int64_t c0 = kt * g.BK, c1 = min<int64_t>(g.N, c0 + g.BK);
-    const int64_t area = rows * (c1 - c0);
-    int64_t cnt;
+  const int N = (int)g.N, iq0 = (int)q0, iq1 = (int)q1, irows = (int)rows, iu = (int)unit;
+  const int v0 = iq0 / iu, v1 = (iq1 - 1) / iu;
+  for (int kt = threadIdx.x; kt < g.nK; kt += kThreads) {
+    const int c0 = kt * g.BK, c1 = min(N, c0 + g.BK);
+    const int area = irows * (c1 - c0);
+    const int C0 = (c0 + g.F - 1) / g.F, C1 = (c1 + g.F - 1) / g.F;
+    int cnt;
     if (kind == SVG_HEAD_DENSE) {
       cnt = area;
     } else {
-      int64_t mask = 0, contig = 0;
-      for (int64_t v = q0 / unit; v <= (q1 - 1) / unit; ++v) {
-        const int64_t len = min(q1, (v + 1) * unit) - max(q0, v * unit);
-        const Counts c = row_columns(g, kind, v, c0, c1);
+      int mask = 0, contig = 0;
+      for (int v = v0; v <= v1; ++v) {
+        const int len = min(iq1, (v + 1) * iu) - max(iq0, v * iu);
+        const Counts c = row_columns(g, kind, v, c0, c1, C0, C1);
         mask += len * c.mask;
         contig += len * c.contig;
       }
@@ -125,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MapGeometry g, MapBu
         if (contig > 0)
           cnt = area;  // the contiguous part is rounded out to the whole tile
         else if (kind == SVG_HEAD_TEMPORAL)
-          cnt = g.sink ? rows * multiples(c0, c1, g.F) : 0;  // exact strided sink
+          cnt = g.sink ? irows * (C1 - C0) : 0;  // exact strided sink
         else
           cnt = 0;
       }
