@@ -21,10 +21,13 @@
 // Schedule. A wave cannot overlap its own MFMAs with its own VALU work, but
 // the two waves of a SIMD can overlap each other's. With eight waves the
 // workgroup forms two groups, one wave of each per SIMD, and every step has
-// two phases separated by a barrier: while group 0 runs the MFMA phase of
-// step t (PV of step t-1, then S^T of step t), group 1 runs the softmax of
-// step t-1; then group 0 runs the softmax of step t while group 1 runs its
-// MFMA phase. All memory work rides in the wave that is otherwise idle
+// two phases: while group 0 runs the MFMA phase of step t (PV of step t-1,
+// then S^T of step t), group 1 runs the softmax of step t-1; then group 0
+// runs the softmax of step t while group 1 runs its MFMA phase. Only a
+// barrier at the end of the step synchronises the groups (the phases share
+// no LDS data), so when one phase runs short the two waves of a SIMD share
+// the matrix pipe instead of one of them waiting. All memory work rides in
+// the wave that is otherwise idle
 // between MFMAs: group 0 issues the next step's loads inside its MFMA phase,
 // group 1 transposes V (reads during its softmax, writes during its MFMA
 // phase). With fewer waves every wave runs both phases in turn.
@@ -361,15 +364,12 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
-// Barrier between the two phases of a step. The scheduler must not move
-// work across it: a barrier orders memory operations only, and softmax work
-// sunk into the MFMA phase (or the reverse) would run on the wave's own
-// VALU beside its MFMAs instead of beside the partner wave's.
-__device__ __forceinline__ void phase_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
+// Border between the two phases of a step: the scheduler must not move work
+// across it, since softmax work sunk into the MFMA phase (or the reverse)
+// would run on the wave's own VALU beside its MFMAs instead of beside the
+// partner wave's. (No barrier: within a step the groups read only the
+// current stage and write only the next one.)
+__device__ __forceinline__ void phase_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
@@ -648,8 +648,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
     // the MFMA phase of step t with the transpose of V of step t into V^T of
     // `nb` woven in. The softmax phases carry no memory work, and the waves
     // of a SIMD alternate: one runs its MFMAs while the other runs its
-    // softmax. A barrier separates the two phases, another closes the
-    // iteration once the loads have landed. Iteration n_steps only finishes
+    // softmax. Within the iteration every LDS read is of `cb`, complete since
+    // the iteration began, and every write is to `nb`, which nobody reads
+    // until the next one, so a single barrier closes the iteration once the
+    // loads and V^T writes have landed. Iteration n_steps only finishes
     // the last PV product (its S^T reads K rows that are not loaded and is
     // never used). One loop per group (the group is a compile-time constant
     // in each), so that the two phase orders are never merged.
@@ -684,7 +686,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
           if (!PP) Stage<D, NW>::transpose(cb, nb, tl, wt);
           st_nn = cur_pos.next(p);
           mphase(cb, DmaSide{stg, Stage<D, NW>::src(p, Kh, Vh, st_next), st_next, nb, wl});
-          if (PP) phase_barrier();
+          if (PP) phase_fence();
           if (has_v) vphase(st_t);
         } else {
           // The transpose reads its V rows at the start of the softmax phase
@@ -696,7 +698,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
           for (int j = 0; j < Lt::TPW; ++j) trbuf[j] = Stage<D, NW>::tr_read(cb, tl, wt, j);
           st_nn = cur_pos.next(p);
           if (t > 0) vphase(st_prev);
-          phase_barrier();
+          phase_fence();
           // write j after MFMA 4j+2
           struct TrSide {
             char* nb;
