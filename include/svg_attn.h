@@ -153,7 +153,9 @@ svg_status svg_build_tile_map(const svg_mask_spec* spec, int32_t tile_q,
                               svg_tile_map** out);
 
 /* Recompute the class map and schedule of an existing map in place, with no
- * allocation (the same kernels as svg_build_tile_map). */
+ * allocation (the same kernels as svg_build_tile_map), on `stream` of the
+ * map's device, which must be current. Errors: INVALID_ARG (null map, other
+ * device current), HIP. */
 svg_status svg_tile_map_rebuild(svg_tile_map* map, void* stream);
 
 /* Sizes of a map. Host-only, no HIP call. */
@@ -190,11 +192,13 @@ svg_status svg_tile_map_destroy(svg_tile_map* map);
  *   head_dim:   64 or 128. scale > 0 and finite (normally 1/sqrt(head_dim)).
  *               One head (seq_len * head_dim * 2 bytes) must be under 2 GiB.
  *   head_kind:  host [num_heads]; must equal the kinds the map was built with.
- *   map:        built for the same seq_len and num_heads.
+ *   map:        built for the same seq_len and num_heads, on the current
+ *               device (its buffers live there).
  *   flags:      0 or SVG_ATTN_MASK_ALL_TILES.
  * Rows with no retained key would give 0 (the masks here always keep one).
- * Errors: INVALID_ARG, UNSUPPORTED (head_dim, head size), SHAPE_MISMATCH (seq_len,
- * num_heads, head kinds vs the map), ALIGNMENT, HIP (launch failure). */
+ * Errors: INVALID_ARG (also: the current device is not the map's),
+ * UNSUPPORTED (head_dim, head size), SHAPE_MISMATCH (seq_len, num_heads, head
+ * kinds vs the map), ALIGNMENT, HIP (launch failure). */
 svg_status svg_attn_fwd(const void* q, const void* k, const void* v, void* o,
                         int64_t seq_len, int32_t num_heads, int32_t head_dim,
                         float scale, const int32_t* head_kind,

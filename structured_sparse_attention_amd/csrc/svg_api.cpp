@@ -64,6 +64,18 @@ svg_status wait_built(const svg_tile_map* m) {
   return SVG_OK;
 }
 
+// The map's buffers live on the device it was built on; its kernels must run
+// there.
+svg_status check_device(const svg_tile_map* m) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != m->device)
+    return fail(SVG_ERR_INVALID_ARG, "the map was built on device %d, the current device is %d",
+                m->device, dev);
+  return SVG_OK;
+}
+
 svg_status run_build(svg_tile_map* m, hipStream_t stream) {
   hipError_t e = svg::launch_build_tile_map(m->geom, m->buf, stream);
   if (e != hipSuccess) return hip_fail(e, "tile-map kernels");
@@ -180,6 +192,8 @@ svg_status svg_build_tile_map(const svg_mask_spec* spec, int32_t tile_q, int32_t
 
 svg_status svg_tile_map_rebuild(svg_tile_map* map, void* stream) {
   if (!map) return fail(SVG_ERR_INVALID_ARG, "map is NULL");
+  const svg_status s = check_device(map);
+  if (s != SVG_OK) return s;
   return run_build(map, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -310,6 +324,8 @@ svg_status svg_attn_fwd(const void* q, const void* k, const void* v, void* o, in
     if (ob < ib + bytes && ib < ob + bytes)
       return fail(SVG_ERR_INVALID_ARG, "o overlaps an input");
   }
+  const svg_status ds = check_device(map);
+  if (ds != SVG_OK) return ds;
   svg::AttnArgs a{q, k, v, o, head_dim, scale, flags};
   const hipError_t e = svg::launch_attn_fwd(g, map->buf, a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
