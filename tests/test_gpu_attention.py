@@ -81,6 +81,40 @@ def test_full_output_parity_small(w):
         check(o, ref, f"flags={flags}")
 
 
+def _ramp_inputs(w, seed):
+    """Scores that ramp along the original key index: each head has a random
+    direction u, row i has Q_i = sign_i u and key j has K_j = t_j u (plus a
+    little noise), with t_j rising over the sequence so that a row's scores
+    span about 60 in log2 units. Rows with sign +1 see their running maximum
+    grow past the lazy rescale bound again and again as the kernel walks its
+    tiles; rows with sign -1 find their maximum in the first tiles and then
+    only smaller values (exponentials that underflow to zero)."""
+    rng = np.random.default_rng(seed)
+    H, N, d = w.num_heads, w.seq_len, w.head_dim
+    span = 60.0 / (np.log2(np.e) * np.sqrt(d))  # raw-score range / |u|^2
+    t = np.arange(N) / N * span
+    Q = np.empty((H, N, d), np.float32)
+    K = np.empty((H, N, d), np.float32)
+    for h in range(H):
+        u = rng.standard_normal(d).astype(np.float32)
+        sign = rng.choice([-1.0, 1.0], size=N).astype(np.float32)
+        Q[h] = sign[:, None] * u[None, :] + 0.1 * rng.standard_normal((N, d))
+        K[h] = t[:, None] * u[None, :] + 0.1 * rng.standard_normal((N, d))
+    V = rng.standard_normal((H, N, d)).astype(np.float32)
+    return tuple(si.f32_to_bf16_bits(x) for x in (Q, K, V))
+
+
+@pytest.mark.parametrize("name", ["tiny-misaligned", "d128-multi-tile", "d128-ragged"])
+def test_lazy_rescale_on_ramping_scores(name):
+    w = {x.name: x for x in SMALL}[name] if name != "tiny-misaligned" else \
+        si.workload("tiny-misaligned")
+    say(f"[attn-ramp] {w.name} N={w.seq_len} d={w.head_dim} BQ={w.tile_q} BK={w.tile_k}")
+    Q, K, V = _ramp_inputs(w, seed=77)
+    ref = oracle.attention(widen(Q), widen(K), widen(V), masks_of(w))
+    for flags in (0, svg.ATTN_MASK_ALL_TILES):
+        check(run_attention(w, Q, K, V, flags=flags), ref, f"ramp flags={flags}")
+
+
 def _sample_rows(w, n, seed=123):
     rng = np.random.default_rng(seed)
     N = w.seq_len
