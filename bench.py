@@ -13,7 +13,8 @@ Prints one JSON line. `value` is effective TFLOP/s over retained pairs
 attention kernel alone (HIP events around each launch on the launch stream),
 the tile-map build, the same-shape dense run through the same kernel, the
 naive traversal (mask evaluated on every executed tile), the tile-aligned
-variant, the 1440p workload (302,400 tokens), a tile-size search (svg_autotune_tiles) over {128, 256, 512} x {64,
+variant, the 1440p workload (302,400 tokens), the token permutation of one
+tensor (GB/s), a tile-size search (svg_autotune_tiles) over {128, 256, 512} x {64,
 128, 256}, sampled head routing (svg_route_heads; not part of the step, as on
 the pages) and a plain bf16 GEMM for reference; "cpu_baseline" times the float64
 oracle on a bounded sample.
@@ -310,6 +311,24 @@ def main():
         extra["tile_aligned_tflops_rounded_mask"] = round(
             4.0 * w.head_dim * tpairs / (np.mean(tattn) * 1e-3) / 1e12, 1)
         log(f"[bench] tile-aligned {np.mean(tattn):.3f} ms (pairs {tpairs / pairs - 1:+.3%})")
+        # token permutation (outside the step, as on the pages): all heads of
+        # one tensor to the kernel layout; HBM-bound, bytes = 2 * H * N * d * 2
+        stream = torch.cuda.current_stream()
+        pev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        svg.svg_permute_tokens(q, o, w.frames, w.tokens_per_frame, w.head_kinds,
+                               svg.TO_KERNEL_LAYOUT)
+        pev[0].record(stream)
+        for _ in range(10):
+            svg.svg_permute_tokens(q, o, w.frames, w.tokens_per_frame, w.head_kinds,
+                                   svg.TO_KERNEL_LAYOUT)
+        pev[1].record(stream)
+        torch.cuda.synchronize()
+        pms = pev[0].elapsed_time(pev[1]) / 10
+        pbytes = 2 * w.num_heads * w.seq_len * w.head_dim * 2
+        extra["permute_tensor_ms"] = round(pms, 4)
+        extra["permute_gbps"] = round(pbytes / (pms * 1e-3) / 1e9, 1)
+        log(f"[bench] permute one tensor ({pbytes / 1e6:.0f} MB moved) {pms:.4f} ms, "
+            f"{extra['permute_gbps']} GB/s")
         extra["routing"] = routing_times(w, host)
         cands = [(bq, bk) for bq in (128, 256, 512) for bk in (64, 128, 256)]
         best, cms = svg.svg_autotune_tiles(q, k, v, o, w.frames, w.grid_h, w.grid_w,

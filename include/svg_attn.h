@@ -260,7 +260,10 @@ svg_status svg_route_heads(const svg_mask_spec* spec, const void* q,
  * each head's kernel layout (temporal heads: p = s*F + f; other heads: p = t,
  * a plain copy). src, dst: device bf16 [num_heads][frames*tokens_per_frame]
  * [head_dim], 16-byte aligned, not overlapping. head_dim a multiple of 8, at
- * most 1024. head_kind: host [num_heads]. */
+ * most 1024; one head (frames * tokens_per_frame * head_dim * 2 bytes) under
+ * 2 GiB. head_kind: host [num_heads]. Queued on `stream` (one launch per run
+ * of consecutive heads of one kind). Errors: INVALID_ARG, UNSUPPORTED
+ * (head_dim, head size), ALIGNMENT, HIP. */
 svg_status svg_permute_tokens(const void* src, void* dst, int32_t frames,
                               int32_t tokens_per_frame, int32_t num_heads,
                               int32_t head_dim, const int32_t* head_kind,

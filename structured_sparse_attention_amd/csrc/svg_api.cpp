@@ -342,6 +342,9 @@ svg_status svg_permute_tokens(const void* src, void* dst, int32_t frames,
     return fail(SVG_ERR_INVALID_ARG, "sequence exceeds 2^30 tokens");
   if (head_dim < 8 || head_dim > 1024 || head_dim % 8)
     return fail(SVG_ERR_UNSUPPORTED, "head_dim %d: multiples of 8 up to 1024", head_dim);
+  if ((int64_t)frames * tokens_per_frame * head_dim * 2 >= ((int64_t)1 << 31))
+    return fail(SVG_ERR_UNSUPPORTED, "one head of %lld x %d bf16 values exceeds 2 GiB",
+                (long long)frames * tokens_per_frame, head_dim);
   if (direction != SVG_TO_KERNEL_LAYOUT && direction != SVG_TO_ORIGINAL_LAYOUT)
     return fail(SVG_ERR_INVALID_ARG, "direction %d is not an svg_permute_dir", direction);
   for (int32_t h = 0; h < num_heads; ++h) {

@@ -170,6 +170,7 @@ def test_permute_rejects_bad_arguments_before_hip(lib):
     assert f(None, b, 4, 64, 2, 64, kp, 0, None) == svg.ERR_INVALID_ARG
     assert f(a, b, 0, 64, 2, 64, kp, 0, None) == svg.ERR_INVALID_ARG
     assert f(a, b, 4, 64, 2, 60, kp, 0, None) == svg.ERR_UNSUPPORTED
+    assert f(a, b, 1 << 12, 1 << 12, 2, 64, kp, 0, None) == svg.ERR_UNSUPPORTED  # head >= 2 GiB
     assert f(a, b, 4, 64, 2, 64, kp, 2, None) == svg.ERR_INVALID_ARG
     assert f(a + 8, b, 4, 64, 2, 64, kp, 0, None) == svg.ERR_ALIGNMENT
     assert f(a, a + 16, 4, 64, 2, 64, kp, 0, None) == svg.ERR_INVALID_ARG  # overlap
