@@ -419,8 +419,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
   const typename Stage<D, NW>::TrLane tl = Stage<D, NW>::tr_lane(lane);
   Stage<D, NW> stg;
   if (loader) stg.init(wl, lane, p.F);
-  // Stage 0 holds the first step's K and V rows; its V^T area holds zeros,
-  // which the first MFMA phase multiplies by P = 0.
+  // Stage 0's V^T area starts as zeros, which the first MFMA phase
+  // multiplies by P = 0. The V rows of both stages start as zeros too: a
+  // row past the sequence reads as zero, and should its LDS slot be left
+  // unwritten instead, the slot still holds a finite value (zero or an
+  // earlier row), so that P = 0 times it stays 0 in O.
+  for (int off = threadIdx.x * 16; off < Lt::VTILE; off += NW * 64 * 16)
+    *(uint4*)(buf0 + Lt::VT_OFF + off) = make_uint4(0, 0, 0, 0);
+  for (int off = threadIdx.x * 16; off < Lt::KTILE; off += NW * 64 * 16) {
+    *(uint4*)(buf0 + Lt::VR_OFF + off) = make_uint4(0, 0, 0, 0);
+    *(uint4*)(buf1 + Lt::VR_OFF + off) = make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();  // the zeros land before any load writes LDS
+  // Stage 0 holds the first step's K and V rows.
   Cursor cur_pos;
   cur_pos.init(p.entries + ebeg, n_tiles, n_full, n_s1, sa, sb, lane);
   Step st_t = {0, 1, 0, 0};
@@ -431,8 +442,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
       for (int j = 0; j < Lt::LPW; ++j)
         stg.load(Stage<D, NW>::src(p, Kh, Vh, st_t), st_t, buf0, wl, j);
   }
-  for (int off = threadIdx.x * 16; off < Lt::VTILE; off += NW * 64 * 16)
-    *(uint4*)(buf0 + Lt::VT_OFF + off) = make_uint4(0, 0, 0, 0);
 
   // ---- Q fragments (B operand of S^T = K Q^T) and this lane's mask bounds.
   const int q = wg_q + wave * QW + l32;
