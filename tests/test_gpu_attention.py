@@ -67,7 +67,13 @@ SMALL = [si.workload("tiny"), si.workload("tiny-misaligned"), RAGGED, RAGGED_NOS
          si.Workload("d128-ragged", 5, 9, 10, ("spatial", "temporal", "dense", "temporal"), 128,
                      1, 13, True, 256, 128, False, seed=35),
          si.Workload("d128-multi-tile", 6, 12, 16, ("spatial", "temporal"), 128, 1, 40, True,
-                     256, 128, False, seed=36)]
+                     256, 128, False, seed=36),
+         # d = 128 with one and two waves per workgroup (every wave loads,
+         # transposes and computes)
+         si.Workload("d128-bq32", 5, 9, 10, ("spatial", "temporal", "dense"), 128, 1, 13, True,
+                     32, 64, False, seed=38),
+         si.Workload("d128-bq64", 4, 7, 11, ("spatial", "temporal"), 128, 1, 9, True,
+                     64, 32, False, seed=39)]
 
 
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: f"{w.name}@{w.tile_q}x{w.tile_k}")
