@@ -27,10 +27,10 @@
 // barrier at the end of the step synchronises the groups (the phases share
 // no LDS data), so when one phase runs short the two waves of a SIMD share
 // the matrix pipe instead of one of them waiting. All memory work rides in
-// the wave that is otherwise idle
-// between MFMAs: group 0 issues the next step's loads inside its MFMA phase,
-// group 1 transposes V (reads during its softmax, writes during its MFMA
-// phase). With fewer waves every wave runs both phases in turn.
+// the wave that is otherwise idle between MFMAs: group 0 issues the next
+// step's loads inside its MFMA phase, group 1 transposes V (reads during its
+// softmax, writes during its MFMA phase). With fewer waves every wave runs
+// both phases in turn.
 //
 // Staging. K rows and V rows move from HBM straight into LDS (buffer_load
 // ... lds, no VGPRs), one step ahead, into two buffers used in turn. V is
@@ -185,14 +185,14 @@ __device__ __forceinline__ Step make_step(const KParams& p, int ti, int bnd, int
 // Staging of one step. K rows and V rows move from HBM straight into LDS
 // (buffer_load ... lds, no VGPRs), both in the same padded row layout (LDS
 // row m of a 32-row K block holds key sigma(m); LDS row m of V holds key
-// vkey(m)). The (row,
-// chunk) a lane fetches in load j is fixed, so its byte offset from the
-// step's first row is too: one table for steps of consecutive rows, one for
-// sink steps at a stride of F rows. The step's first row goes into the base
-// of the buffer resources, whose record count ends at the end of the
-// sequence: rows past it read as zeros (the buffer range check), rows past
-// the step's column count are masked, and a load costs no address
-// arithmetic. Pad slots re-read chunk 0 of their row (never read back).
+// vkey(m)). The (row, chunk) a lane fetches in load j is fixed, so its byte
+// offset from the step's first row is too: one table for steps of
+// consecutive rows, one for sink steps at a stride of F rows. The step's
+// first row goes into the base of the buffer resources, whose record count
+// ends at the end of the sequence: rows past it read as zeros (the buffer
+// range check), rows past the step's column count are masked, and a load
+// costs no address arithmetic. Pad slots re-read chunk 0 of their row (never
+// read back).
 //
 // V is then transposed inside LDS once per step: each 16-lane group reads 4
 // keys x 16 dims with one ds_read_b64_tr_b16 (lane j gets dim j of the 4
