@@ -74,6 +74,9 @@ SMALL = [si.workload("tiny"), si.workload("tiny-misaligned"), RAGGED, RAGGED_NOS
                      32, 64, False, seed=38),
          si.Workload("d128-bq64", 4, 7, 11, ("spatial", "temporal"), 128, 1, 9, True,
                      64, 32, False, seed=39)]
+# the tile-aligned mask on the degenerate shapes: zero windows without the
+# sink, windows wider than the sequence, a single frame
+SMALL += [_aligned(w) for w in SMALL if w.name in ("narrow", "wide", "one-frame")]
 
 
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: f"{w.name}@{w.tile_q}x{w.tile_k}")

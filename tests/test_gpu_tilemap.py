@@ -46,6 +46,11 @@ def _small_workloads():
                            64, 96, False, seed=33))
     out.append(si.Workload("narrow", 6, 4, 5, ("spatial", "temporal"), 64, 0, 0, False,
                            32, 64, False, seed=34))
+    # the same degenerate shapes with the tile-aligned mask
+    for w in list(out[-4:]):
+        out.append(si.Workload(w.name + "-ta", w.frames, w.grid_h, w.grid_w, w.head_kinds,
+                               w.head_dim, w.frame_window, w.band, w.sink, w.tile_q,
+                               w.tile_k, True, w.seed))
     return out
 
 
