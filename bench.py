@@ -310,6 +310,8 @@ def main():
         extra["tile_aligned_pairs_drift"] = round(tpairs / pairs - 1.0, 5)
         extra["tile_aligned_tflops_rounded_mask"] = round(
             4.0 * w.head_dim * tpairs / (np.mean(tattn) * 1e-3) / 1e12, 1)
+        extra["tile_aligned_tflops_exact_mask"] = round(
+            4.0 * w.head_dim * pairs / (np.mean(tattn) * 1e-3) / 1e12, 1)
         log(f"[bench] tile-aligned {np.mean(tattn):.3f} ms (pairs {tpairs / pairs - 1:+.3%})")
         # token permutation (outside the step, as on the pages): all heads of
         # one tensor to the kernel layout; HBM-bound, bytes = 2 * H * N * d * 2
