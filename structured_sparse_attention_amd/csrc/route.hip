@@ -391,13 +391,37 @@ __global__ __launch_bounds__(256) void route_decide(RouteParams p, const double*
 
 }  // namespace
 
-RouteLayout route_layout(int64_t N, int32_t H, int32_t D, int32_t n_rows) {
+int route_slots(int32_t D) {
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const void* f = D == 128 ? reinterpret_cast<const void*>(&route_partial<128>)
+                           : reinterpret_cast<const void*>(&route_partial<64>);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, f, RW * 64, 0) != hipSuccess) return 0;
+  return cus * per;
+}
+
+RouteLayout route_layout(int64_t N, int32_t H, int32_t D, int32_t n_rows, int32_t slots) {
   RouteLayout L;
   L.pitch = (N + 63) / 64 * 64 + 64;  // a multiple of 64; keys past N read zeros
   const int64_t pairs = ((n_rows + RQ - 1) / RQ + 1) / 2;  // workgroups per (head, split)
-  // about 4096 waves in all
-  int64_t ns = (4096 + RW * H * pairs - 1) / (RW * H * pairs);
-  ns = std::max<int64_t>(1, std::min<int64_t>(ns, (N + RK - 1) / RK));
+  // Key splits. The time is about (rounds of resident workgroups) x (keys
+  // per split), so take the split count that minimises rounds / splits, up
+  // to about two rounds of workgroups (more splits cost partial results and
+  // merging), the fewest on a tie: no partial last round idles most of the
+  // chip. Without the occupancy figure, about 4096 waves in all.
+  const int64_t per = (int64_t)H * pairs, kmax = (N + RK - 1) / RK;
+  int64_t ns = (4096 + RW * per - 1) / (RW * per);
+  if (slots > 0) {
+    const int64_t hi = std::max<int64_t>(1, std::min<int64_t>(kmax, (2 * slots + per - 1) / per));
+    ns = 1;
+    for (int64_t c = 2; c <= hi; ++c) {
+      const int64_t r = (c * per + slots - 1) / slots, rb = (ns * per + slots - 1) / slots;
+      if (r * ns < rb * c) ns = c;  // r / c < rb / ns
+    }
+  }
+  ns = std::max<int64_t>(1, std::min<int64_t>(ns, kmax));
   L.split_len = ((N + ns - 1) / ns + RK - 1) / RK * RK;
   L.n_split = (N + L.split_len - 1) / L.split_len;
   const int64_t a = 256;

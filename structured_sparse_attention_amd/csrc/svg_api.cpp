@@ -458,7 +458,7 @@ svg_status svg_route_heads(const svg_mask_spec* spec, const void* q, const void*
   if (!aligned16(q) || !aligned16(k) || !aligned16(v))
     return fail(SVG_ERR_ALIGNMENT, "q, k and v must be 16-byte aligned");
   const int32_t H = spec->num_heads;
-  const svg::RouteLayout L = svg::route_layout(N, H, head_dim, n_rows);
+  const svg::RouteLayout L = svg::route_layout(N, H, head_dim, n_rows, svg::route_slots(head_dim));
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* scratch = nullptr;
   hipError_t e = hipMalloc(reinterpret_cast<void**>(&scratch), (size_t)L.bytes);

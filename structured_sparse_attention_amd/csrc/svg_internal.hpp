@@ -62,7 +62,11 @@ struct RouteLayout {
   int64_t n_split;
   int64_t vt_off, rows_off, part_off, row_err_off, err_off, kind_off, bytes;
 };
-RouteLayout route_layout(int64_t N, int32_t H, int32_t D, int32_t n_rows);
+// slots: workgroups of the routing kernel the device holds at once (0 if
+// unknown), which sets the number of key splits.
+RouteLayout route_layout(int64_t N, int32_t H, int32_t D, int32_t n_rows, int32_t slots);
+// CUs x resident routing workgroups per CU on the current device, 0 on failure.
+int route_slots(int32_t D);
 // Queue the routing kernels; the sampled rows must already be at
 // scratch + rows_off. Results: float [H][2] at err_off, int32 [H] at kind_off.
 hipError_t launch_route(const void* q, const void* k, const void* v, char* scratch,
