@@ -43,8 +43,6 @@ hipError_t launch_permute_tokens(const void* src, void* dst, int32_t F, int32_t 
                                  int32_t direction, hipStream_t stream) {
   const int32_t chunks = D / 8;
   const int64_t per_head = (int64_t)F * S * chunks;
-  // enough blocks to fill the chip twice over per launch, at most one chunk
-  // per thread
   auto mode_of = [&](int32_t h) {
     return kinds[h] == SVG_HEAD_TEMPORAL ? (direction == SVG_TO_KERNEL_LAYOUT ? 1 : 2) : 0;
   };
@@ -53,7 +51,10 @@ hipError_t launch_permute_tokens(const void* src, void* dst, int32_t F, int32_t 
     const int32_t mode = mode_of(h0);
     int32_t h1 = h0 + 1;
     while (h1 < H && mode_of(h1) == mode && h1 - h0 < 65535) ++h1;
-    const int64_t want = (2 * 256 * 8 + (h1 - h0) - 1) / (h1 - h0);  // blocks per head
+    // about 16,384 blocks per launch (64 per CU on a 256-CU part), at most
+    // one per 256 chunks: fewer blocks left HBM bandwidth unused (5.26 TB/s
+    // with 4,096 against 5.50 with 16,384 on the main workload)
+    const int64_t want = (16384 + (h1 - h0) - 1) / (h1 - h0);  // blocks per head
     const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((per_head + 255) / 256, want));
     const uint4* s = (const uint4*)src + (int64_t)h0 * per_head;
     uint4* d = (uint4*)dst + (int64_t)h0 * per_head;
