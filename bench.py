@@ -19,9 +19,9 @@ tensor (GB/s), a tile-size search (svg_autotune_tiles) over {128, 256, 512} x {6
 the pages) and a plain bf16 GEMM for reference; "cpu_baseline" times the float64
 oracle on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
                     [--no-extras] [--cpu-rows 12288] [--profile] [--copy-calibration]
-                    [--routing-only]
+                    [--routing-only] [--workload main|dense|tile-aligned|1440p]
 """
 from __future__ import annotations
 
@@ -53,14 +53,14 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="main")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the dense, naive and tile-aligned runs")
     ap.add_argument("--cpu-rows", type=int, default=12288, help="oracle query rows per head")
     ap.add_argument("--profile", action="store_true",
-                    help="few steps, main workload only (for rocprofv3)")
+                    help="the timed steps only, no extras and no CPU baseline (for rocprofv3)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--routing-only", action="store_true",
@@ -100,7 +100,8 @@ def device_inputs(w):
 def time_steps(w, q, k, v, o, steps, warmup, flags=0):
     """Time `steps` steps (map rebuild + attention) on the current stream.
 
-    Returns (ms per step, attention-kernel ms list, map ms list, per-head stats).
+    Returns (ms per step, attention-kernel ms list, map ms list, per-head
+    stats, launch-plan statistics).
     """
     import torch
     import structured_sparse_attention_amd as svg
@@ -108,6 +109,7 @@ def time_steps(w, q, k, v, o, steps, warmup, flags=0):
         w.frames, w.grid_h, w.grid_w, w.head_kinds, w.frame_window, w.band, w.sink,
         svg.ROUND_TILE if w.tile_aligned else svg.ROUND_EXACT, w.tile_q, w.tile_k)
     stats = tm.stats()
+    plan = tm.plan_info()
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         tm.rebuild(stream)
@@ -129,7 +131,7 @@ def time_steps(w, q, k, v, o, steps, warmup, flags=0):
     attn = [e[1].elapsed_time(e[2]) for e in ev]
     amap = [e[0].elapsed_time(e[1]) for e in ev]
     tm.destroy()
-    return total / steps, attn, amap, stats
+    return total / steps, attn, amap, stats, plan
 
 
 # ------------------------------------------------------------------ CPU oracle
@@ -180,11 +182,15 @@ def cpu_baseline(w, Q, K, V, rows_per_head):
     if limit is not None:
         limit.restore_original_limits()
     tflops = 4.0 * w.head_dim * pairs / dt / 1e12
+    full_s = dt * w.seq_len / rows_per_head
     return {"value": tflops, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"{rows_per_head} query rows x {w.num_heads} heads of the {w.name} "
-                      f"workload against all {w.seq_len} keys: float64 explicit-mask attention, "
-                      f"{pairs} retained pairs, {cores} processes with single-threaded BLAS"}
+            "full_workload_seconds_extrapolated": round(full_s, 1),
+            "sample": f"a row sample, not the whole workload: {rows_per_head} of {w.seq_len} "
+                      f"query rows per head x {w.num_heads} heads of the {w.name} workload, "
+                      f"each against all {w.seq_len} keys (float64 explicit-mask attention, "
+                      f"{pairs} retained pairs, {cores} processes with single-threaded BLAS); "
+                      f"every row would take about {full_s:.0f} s at this rate"}
 
 
 # ------------------------------------------------------------------ routing
@@ -270,13 +276,13 @@ def main():
     import torch
     import seeded_inputs as si
     if a.profile:
-        a.steps, a.warmup, a.no_cpu_baseline, a.no_extras = min(a.steps, 5), 1, True, True
+        a.no_cpu_baseline, a.no_extras = True, True
     w = si.workload(a.workload)
     log(f"[bench] workload {w.name}: N={w.seq_len} H={w.num_heads} d={w.head_dim} "
         f"tiles {w.tile_q}x{w.tile_k}")
     (q, k, v), host = device_inputs(w)
     o = torch.empty_like(q)
-    ms, attn, amap, stats = time_steps(w, q, k, v, o, a.steps, a.warmup)
+    ms, attn, amap, stats, plan = time_steps(w, q, k, v, o, a.steps, a.warmup)
     pairs = sum(s["retained_pairs"] for s in stats)
     flop = 4.0 * w.head_dim * pairs
     value = flop / (ms * 1e-3) / 1e12
@@ -288,6 +294,8 @@ def main():
     extra = {
         "attn_kernel_ms": {"mean": round(attn_ms, 4), "median": round(float(np.median(attn)), 4),
                            "min": round(min(attn), 4)},
+        "launch_plan": dict(plan, busiest_over_mean=round(
+            plan["max_load"] * plan["workgroups"] / max(1, plan["total_load"]), 4)),
         "tile_map_ms": round(float(np.mean(amap)), 4),
         "retained_pairs": pairs,
         "exec_tiles_full_boundary_sink": [sum(s["exec_full"] for s in stats),
@@ -300,11 +308,11 @@ def main():
     if not a.no_extras and w.name == "main":
         import structured_sparse_attention_amd as svg
         n_extra = max(3, a.steps // 4)
-        _, nattn, _, _ = time_steps(w, q, k, v, o, n_extra, 1, flags=svg.ATTN_MASK_ALL_TILES)
+        _, nattn, _, _, _ = time_steps(w, q, k, v, o, n_extra, 1, flags=svg.ATTN_MASK_ALL_TILES)
         extra["naive_mask_all_tiles_ms"] = round(float(np.mean(nattn)), 4)
         log(f"[bench] naive (mask every executed tile) {np.mean(nattn):.3f} ms")
         wt = si.workload("tile-aligned")
-        _, tattn, _, tstats = time_steps(wt, q, k, v, o, n_extra, 1)
+        _, tattn, _, tstats, _ = time_steps(wt, q, k, v, o, n_extra, 1)
         tpairs = sum(s["retained_pairs"] for s in tstats)
         extra["tile_aligned_ms"] = round(float(np.mean(tattn)), 4)
         extra["tile_aligned_pairs_drift"] = round(tpairs / pairs - 1.0, 5)
@@ -344,7 +352,7 @@ def main():
         wd = si.workload("dense")
         (qd, kd, vd), _ = device_inputs(wd)
         od = torch.empty_like(qd)
-        dms, dattn, _, dstats = time_steps(wd, qd, kd, vd, od, n_extra, 1)
+        dms, dattn, _, dstats, _ = time_steps(wd, qd, kd, vd, od, n_extra, 1)
         dpairs = sum(s["retained_pairs"] for s in dstats)
         extra["dense_attn_kernel_ms"] = round(float(np.mean(dattn)), 4)
         extra["dense_tflops"] = round(4.0 * wd.head_dim * dpairs
@@ -356,7 +364,7 @@ def main():
         wl = si.workload("1440p")
         (ql, kl, vl), _ = device_inputs(wl)
         ol = torch.empty_like(ql)
-        _, lattn, lmap, lstats = time_steps(wl, ql, kl, vl, ol, 3, 1)
+        _, lattn, lmap, lstats, _ = time_steps(wl, ql, kl, vl, ol, 3, 1)
         lpairs = sum(s["retained_pairs"] for s in lstats)
         extra["1440p_attn_kernel_ms"] = round(float(np.mean(lattn)), 3)
         extra["1440p_tile_map_ms"] = round(float(np.mean(lmap)), 4)

@@ -140,12 +140,34 @@ typedef struct svg_head_stats {
   int64_t retained_pairs; /* |M| (exact) or |M'| (tile-aligned)               */
 } svg_head_stats;
 
+/* Statistics of the map's launch plan (see svg_build_tile_map). Loads are in
+ * 64-key steps plus a fixed cost per work item. */
+typedef struct svg_plan_info {
+  int32_t workgroups;     /* persistent workgroups: one per compute unit      */
+  int32_t xcds;           /* workgroup i runs on XCD i mod xcds               */
+  int64_t work_items;     /* items over all workgroups                        */
+  int64_t split_rows;     /* workgroup-sized row slices cut into parts        */
+  int64_t partial_slots;  /* parts of cut slices (partial results written)    */
+  int64_t max_load;       /* cost of the busiest workgroup                    */
+  int64_t total_load;     /* cost summed over the workgroups                  */
+} svg_plan_info;
+
 /* A3+A4: classify every tile of every head and compact, per (head, Q tile),
  * the KV tiles to execute: FULL ids ascending, then BOUNDARY ids ascending,
- * plus the temporal sink split (a, b). Runs HIP kernels on `stream`;
- * allocates the map's device buffers (freed by svg_tile_map_destroy).
- * Supported tile sizes: tile_q in {32, 64, 128} or a multiple of 256;
- * tile_k a multiple of 32 in [32, 1024].
+ * plus the temporal sink split (a, b). Then plan the attention launch: one
+ * workgroup per compute unit, each with a fixed list of work items (a range
+ * of 64-key steps of a workgroup-sized slice of a schedule row); the slices
+ * an XCD works on at one time are neighbouring Q tiles, and the last slices
+ * of each XCD's share are cut between its workgroups so that all of them
+ * end together. The plan is computed on the host from the map's row counts
+ * by a host function queued on `stream` and then copied to the device.
+ * Everything is queued on `stream` and the call returns without waiting.
+ * Allocates the map's device buffers (class map, schedule, plan, and up to
+ * 2 x (compute units) partial results of (query rows of a workgroup) x 128
+ * fp32 values for cut slices: 64 MiB for 256-row workgroups on 256 compute
+ * units) and pinned host staging, all freed by svg_tile_map_destroy.
+ * Supported tile sizes: tile_q in {32, 64, 128} or a multiple of 256 up to
+ * 2^20; tile_k a multiple of 32 in [32, 1024].
  * Errors: INVALID_ARG (null spec/out/head_kind, bad sizes or kinds),
  * UNSUPPORTED (tile sizes), OOM, HIP. On error *out is left unchanged. */
 svg_status svg_build_tile_map(const svg_mask_spec* spec, int32_t tile_q,
@@ -154,7 +176,8 @@ svg_status svg_build_tile_map(const svg_mask_spec* spec, int32_t tile_q,
 
 /* Recompute the class map and schedule of an existing map in place, with no
  * allocation (the same kernels as svg_build_tile_map), on `stream` of the
- * map's device, which must be current. Errors: INVALID_ARG (null map, other
+ * map's device, which must be current. The launch plan depends only on the
+ * mask specification and is kept. Errors: INVALID_ARG (null map, other
  * device current), HIP. */
 svg_status svg_tile_map_rebuild(svg_tile_map* map, void* stream);
 
@@ -181,6 +204,10 @@ svg_status svg_tile_map_copy_classes(const svg_tile_map* map, uint8_t* host,
 svg_status svg_tile_map_copy_schedule(const svg_tile_map* map, int32_t* row_ptr,
                                       int32_t* n_full, int32_t* sink_ab,
                                       int32_t* entries, size_t n_entries);
+
+/* Statistics of the map's launch plan. Waits for the build. Errors:
+ * INVALID_ARG (null pointers), HIP. */
+svg_status svg_tile_map_plan_info(const svg_tile_map* map, svg_plan_info* out);
 
 /* Free a map (NULL is accepted). Waits for work queued on its build stream. */
 svg_status svg_tile_map_destroy(svg_tile_map* map);

@@ -36,7 +36,7 @@ _KIND_NAMES = {"spatial": HEAD_SPATIAL, "temporal": HEAD_TEMPORAL, "dense": HEAD
 EXPORTED = (
     "svg_build_tile_map", "svg_tile_map_rebuild", "svg_tile_map_info_get",
     "svg_tile_map_stats", "svg_tile_map_copy_classes", "svg_tile_map_copy_schedule",
-    "svg_tile_map_destroy", "svg_attn_fwd", "svg_autotune_tiles", "svg_route_heads",
+    "svg_tile_map_plan_info", "svg_tile_map_destroy", "svg_attn_fwd", "svg_autotune_tiles", "svg_route_heads",
     "svg_permute_tokens", "svg_last_error", "svg_abi_version",
 )
 
@@ -72,6 +72,12 @@ class HeadStats(ctypes.Structure):
         "exec_sink", "retained_pairs")]
 
 
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("workgroups", ctypes.c_int32), ("xcds", ctypes.c_int32)] + [
+        (n, ctypes.c_int64) for n in ("work_items", "split_rows", "partial_slots", "max_load",
+                                      "total_load")]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -93,6 +99,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "svg_tile_map_stats": (I32, [P, ctypes.POINTER(HeadStats), I32]),
         "svg_tile_map_copy_classes": (I32, [P, ctypes.POINTER(ctypes.c_uint8), SZ]),
         "svg_tile_map_copy_schedule": (I32, [P, pI32, pI32, pI32, pI32, SZ]),
+        "svg_tile_map_plan_info": (I32, [P, ctypes.POINTER(PlanInfo)]),
         "svg_tile_map_destroy": (I32, [P]),
         "svg_attn_fwd": (I32, [P, P, P, P, I64, I32, I32, ctypes.c_float, pI32, P, U32, P]),
         "svg_autotune_tiles": (I32, [ctypes.POINTER(MaskSpec), P, P, P, P, I32, ctypes.c_float,
@@ -179,6 +186,11 @@ class TileMap:
                                                  _i32p(sink_ab), _i32p(entries), entries.size))
         return row_ptr, n_full, sink_ab, entries[: int(row_ptr[-1])]
 
+    def plan_info(self) -> dict:
+        pi = PlanInfo()
+        _check(load().svg_tile_map_plan_info(self.handle, ctypes.byref(pi)))
+        return {f: getattr(pi, f) for f, _ in PlanInfo._fields_}
+
     def destroy(self) -> None:
         if self._h:
             _check(load().svg_tile_map_destroy(self._h))
@@ -222,6 +234,8 @@ def svg_attn_fwd(q, k, v, o, head_kind: Sequence[Union[str, int]], tile_map: Til
         if tuple(t.shape) != (H, N, d):
             raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {(H, N, d)}")
     kinds = _kinds(head_kind)
+    if len(kinds) != H:
+        raise ValueError(f"head_kind has {len(kinds)} entries, q has {H} heads")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     _check(load().svg_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), N, H, d,
@@ -299,6 +313,8 @@ def svg_permute_tokens(src, dst, frames: int, tokens_per_frame: int,
     if tuple(dst.shape) != (H, N, d) or N != frames * tokens_per_frame:
         raise ValueError("src/dst shapes disagree with frames * tokens_per_frame")
     kinds = _kinds(head_kind)
+    if len(kinds) != H:
+        raise ValueError(f"head_kind has {len(kinds)} entries, src has {H} heads")
     _check(load().svg_permute_tokens(src.data_ptr(), dst.data_ptr(), frames, tokens_per_frame,
                                      H, d, _i32p(kinds), direction, _stream(stream)))
 

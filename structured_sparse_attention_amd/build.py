@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsvgattn.so")
 
-SOURCES = ["svg_api.cpp", "tilemap.hip", "attn_fwd.hip", "permute.hip", "route.hip"]
+SOURCES = ["svg_api.cpp", "plan.cpp", "tilemap.hip", "attn_fwd.hip", "permute.hip", "route.hip"]
 ARCH = os.environ.get("SVG_OFFLOAD_ARCH", "gfx950")
 
 # Packed FP32 instructions are kept out of the generated code on purpose.

@@ -44,12 +44,19 @@
 // that keeps the transposing reads free of bank conflicts. A step's first
 // row is folded into the base of its buffer resources, so the loads need no
 // per-lane address arithmetic and rows past the sequence read as zeros.
-// Workgroups are remapped so that consecutive Q tiles of a head run on the
-// same XCD and share its L2, in blocks dealt out in rounds so that the XCDs
-// stay balanced.
+//
+// Dispatch. The launch is persistent: one workgroup per compute unit, each
+// walking the list of work items that the map's plan gave it (plan.hpp): a
+// work item is a range of steps of one workgroup-sized slice of a schedule
+// row. The plan keeps the Q tiles an XCD works on at one time neighbours
+// (they share their KV tiles in its L2) and ends every workgroup level by
+// cutting the last rows of each XCD's band between workgroups. A cut row's
+// parts write their unnormalised O, running maximum and row sum to partial
+// slots, and combine_kernel merges them after the launch.
 #include "svg_internal.hpp"
 
 #include <math.h>
+#include <stddef.h>
 
 #include <type_traits>
 
@@ -99,16 +106,39 @@ struct KParams {
   const uint16_t* v;
   uint16_t* o;
   int32_t N, F, S, W_f, W_s, sink;
-  int32_t BQ, BK, nQ, nsub, total_wg, cpt;
-  const int32_t* kinds;
-  const int32_t* rowinfo;
-  const int32_t* row_ptr;
+  int32_t BQ, BK, nQ, nsub, cpt;
   const int32_t* entries;
+  const int32_t* item_ptr;  // per-XCD queue bounds [n_xcd + 1]
+  const int4* items;        // ItemDesc, three int4 each (see svg_internal.hpp)
+  int32_t* counters;        // this launch's queue positions [n_xcd], zeroed
+  int32_t n_xcd;
+  // bounds every plan entry is checked against
+  int32_t H, n_units, max_items, max_slots, n_k_tiles, entry_cap;
+  float* part_o;            // [slot][rows of a workgroup][D], unnormalised O
+  float2* part_ml;          // [slot][rows of a workgroup]: (running max, row sum)
   float c;             // scale * log2(e)
   float thr;           // lazy-rescale threshold in raw score units
   int32_t mask_all;    // evaluate the mask on every executed step
   int32_t round_tile;  // the map rounds the contiguous mask part to whole tiles
 };
+
+// Kernel arguments needed only where a work item starts or ends are read
+// there again, with volatile loads from the argument segment that the
+// compiler cannot hoist: kept live across the step loop they would crowd the
+// scalar registers that the step machinery needs (and spill into vector
+// lanes read back inside the MFMA phase). The kernel's one argument is the
+// KParams struct at offset 0 of the segment.
+template <typename T, size_t OFF>
+__device__ __forceinline__ T kernarg_reload() {
+  typedef __attribute__((address_space(4))) const char* kptr;
+  typedef __attribute__((address_space(4))) const volatile T* vptr;
+  return *(vptr)((kptr)__builtin_amdgcn_kernarg_segment_ptr() + OFF);
+}
+#define ARG(field) (kernarg_reload<decltype(KParams::field), offsetof(KParams, field)>())
+
+// The same for fields of a work item that the item's end needs again.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 reload_int4(const int4* p) { return *(const volatile i32x4*)p; }
 
 struct Step {
   int32_t base;    // kernel-layout row of the step's first key
@@ -132,21 +162,6 @@ __device__ __forceinline__ int sigma(int m) {
 // consecutive rows they would hit the same banks 2 to 4 times).
 __device__ __forceinline__ int vkey(int m) {
   return (m & ~15) | ((m & 3) << 2) | ((m >> 2) & 3);
-}
-
-// Logical workgroup of launch index i (T workgroups). The hardware deals
-// launch indices round-robin over the 8 XCDs; XCD x then takes blocks of XB
-// consecutive logical workgroups (consecutive Q tiles of a head, which share
-// their KV tiles in the XCD's L2) in rounds, block 8r + x in round r, so that
-// every XCD sees a mix of heads and finishes with the others. Workgroups past
-// the last full round are split into contiguous runs, one per XCD.
-constexpr int XB = 16;
-__device__ __forceinline__ int xcd_remap(int i, int T) {
-  const int x = i & 7, j = i >> 3;
-  const int J = XB * (T / (8 * XB));  // per XCD, in full rounds
-  if (j < J) return ((j / XB) * 8 + x) * XB + j % XB;
-  const int jr = j - J, Tr = T - 8 * J, per = Tr >> 3, rem = Tr & 7;
-  return 8 * J + (x < rem ? x * (per + 1) + jr : rem * (per + 1) + (x - rem) * per + jr);
 }
 
 // Values of this lane and of lane ^ 32.
@@ -244,17 +259,18 @@ struct Stage {
 
   // Load pair j (K and V rows of one 1 KiB slot) of step `s` into `buf`,
   // without a branch: a wave that has no load j repeats its load j-1 (the
-  // same bytes to the same place).
-  __device__ __forceinline__ void load(const Src& sr, const Step& s, char* buf, int wl,
+  // same bytes to the same place). wl1k = 1024 * wl, the wave's slot; the
+  // caller launders it once per step, so that the destination of each load
+  // is one scalar add there rather than a register held across the loop.
+  __device__ __forceinline__ void load(const Src& sr, const Step& s, char* buf, int wl, int wl1k,
                                        int j) const {
     // (the tables already hold the repeated load; indices stay compile-time
     // constants, which keeps the tables in registers)
     const bool ok = j == 0 || k_ok(j, wl);
-    const int jj = ok ? j : j - 1;
     const bool one = s.stride == 1;
     const uint32_t ko = one ? koff[j] : koffs[j];
     const uint32_t vo = one ? voff[j] : voffs[j];
-    const int at = (jj * Lt::NL + wl) * 1024;
+    const int at = (ok ? j * Lt::NL * 1024 : (j - 1) * Lt::NL * 1024) + wl1k;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sr.k, (lds_void*)(buf + at), 16, ko, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sr.v, (lds_void*)(buf + Lt::VR_OFF + at), 16, vo,
                                              0, 0, 0);
@@ -262,42 +278,57 @@ struct Stage {
 
   // V rows of `src` -> V^T of `dst` (this transposer wave's share). Chunk
   // c = (t * NT + wt) * 64 + lane is dim c % D of key group c / D; a 16-lane
-  // group covers 16 consecutive dims of one key group. Addresses split into a
-  // per-lane part (fixed) and a wave-uniform part per pass.
+  // group covers 16 consecutive dims of one key group. An address is a
+  // per-lane part, a per-wave part and a per-pass part; the per-wave part is
+  // added to the per-lane base once (it does not depend on the pass, see
+  // tr_split_ok), so that every pass adds a compile-time offset only.
   struct TrLane {
     int rd, wr;
   };
-  __device__ __forceinline__ static TrLane tr_lane(int lane) {
+  __device__ __forceinline__ static TrLane tr_lane(int lane, int wt) {
     const int q = lane >> 4, jj = lane & 15;
-    return {(jj >> 2) * 4 * Lt::KROW + 2 * (16 * q + 4 * (jj & 3)), (16 * q + jj) * Lt::VTROW};
+    return {(jj >> 2) * 4 * Lt::KROW + 2 * (16 * q + 4 * (jj & 3)) + tr_rd(wt, 0, 0) -
+                tr_rd(0, 0, 0),
+            (16 * q + jj) * Lt::VTROW + tr_wr(wt, 0) - tr_wr(0, 0)};
   }
-  // uniform part of pass t: read offsets of keys 8g..8g+3 and 8g+4..8g+7
-  // (key 16a + 4b + i sits in V row 16a + 4i + b) and the write offset
-  __device__ __forceinline__ static int tr_rd(int wt, int t, int half) {
+  // offsets of pass t of wave wt: read offsets of keys 8g..8g+3 and
+  // 8g+4..8g+7 (key 16a + 4b + i sits in V row 16a + 4i + b) and the write
+  // offset
+  __host__ __device__ static constexpr int tr_rd(int wt, int t, int half) {
     const int u = t * Lt::NT + wt, dd = (u % (D / 64)) * 64, g = u / (D / 64);
     const int pr = 16 * (g >> 1) + 2 * (g & 1) + half;
     return Lt::VR_OFF + pr * Lt::KROW + 2 * dd;
   }
-  __device__ __forceinline__ static int tr_wr(int wt, int t) {
+  __host__ __device__ static constexpr int tr_wr(int wt, int t) {
     const int u = t * Lt::NT + wt, dd = (u % (D / 64)) * 64, g = u / (D / 64);
     return Lt::VT_OFF + dd * Lt::VTROW + 16 * g;
   }
-  __device__ __forceinline__ static i16x8 tr_read(const char* src, const TrLane& tl, int wt,
-                                                  int t) {
+  // The offsets split into a wave part and a pass part for every transposer
+  // wave and pass.
+  __host__ __device__ static constexpr bool tr_split_ok() {
+    for (int wt = 0; wt < Lt::NT; ++wt)
+      for (int t = 0; t < Lt::TPW; ++t) {
+        for (int half = 0; half < 2; ++half)
+          if (tr_rd(wt, t, half) != tr_rd(0, t, half) + tr_rd(wt, 0, 0) - tr_rd(0, 0, 0))
+            return false;
+        if (tr_wr(wt, t) != tr_wr(0, t) + tr_wr(wt, 0) - tr_wr(0, 0)) return false;
+      }
+    return true;
+  }
+  __device__ __forceinline__ static i16x8 tr_read(const char* src, const TrLane& tl, int t) {
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(src + tr_rd(wt, t, 0) + tl.rd));
+        (lds_i16x4*)(src + tr_rd(0, t, 0) + tl.rd));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(src + tr_rd(wt, t, 1) + tl.rd));
+        (lds_i16x4*)(src + tr_rd(0, t, 1) + tl.rd));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
-  __device__ __forceinline__ static void tr_write(char* dst, const TrLane& tl, int wt, int t,
+  __device__ __forceinline__ static void tr_write(char* dst, const TrLane& tl, int t,
                                                   const i16x8& x) {
-    *(i16x8*)(dst + tr_wr(wt, t) + tl.wr) = x;
+    *(i16x8*)(dst + tr_wr(0, t) + tl.wr) = x;
   }
-  __device__ __forceinline__ static void transpose(const char* src, char* dst, const TrLane& tl,
-                                                   int wt) {
+  __device__ __forceinline__ static void transpose(const char* src, char* dst, const TrLane& tl) {
 #pragma unroll
-    for (int t = 0; t < Lt::TPW; ++t) tr_write(dst, tl, wt, t, tr_read(src, tl, wt, t));
+    for (int t = 0; t < Lt::TPW; ++t) tr_write(dst, tl, t, tr_read(src, tl, t));
   }
 };
 
@@ -316,17 +347,28 @@ struct Cursor {
     const int idx = c * 64 + lane;
     return idx < n_tiles ? ents[idx] : 0;
   }
+  // Position at step s0 of the row: tile steps (cpt per tile) come first,
+  // then the sink steps.
   __device__ __forceinline__ void init(const int32_t* row_ents, int nt, int nf, int ns1, int a,
-                                       int b, int lane) {
+                                       int b, int lane, int cpt, int s0) {
     ents = row_ents;
     n_tiles = nt;
     n_full = nf;
     n_s1 = ns1;
     sa = a;
     sb = b;
-    chunk = e = part = js = 0;
-    e_cur = load(0, lane);
-    e_nxt = load(1, lane);
+    if (s0 < nt * cpt) {
+      e = s0 / cpt;
+      part = s0 - e * cpt;
+      js = 0;
+    } else {
+      e = nt;
+      part = 0;
+      js = s0 - nt * cpt;
+    }
+    chunk = e >> 6;
+    e_cur = load(chunk, lane);
+    e_nxt = load(chunk + 1, lane);
   }
   // Refill the window when the next step starts a new 64-entry chunk (the
   // only branch of the cursor; rare).
@@ -393,377 +435,514 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
   const int hl = lane >> 5, l32 = lane & 31;
   const int grp = PP && wave >= NW / 2 ? 1 : 0;
 
-  const int L = xcd_remap(blockIdx.x, p.total_wg);
-  const int row = L / p.nsub, sub = L - row * p.nsub;
-  const int h = row / p.nQ, qt = row - h * p.nQ;
-  const int wg_q = qt * p.BQ + sub * WGQ;
-  if (wg_q >= p.N) return;  // whole workgroup past a ragged last Q tile
-  const int kind = p.kinds[h];
-
-  const int32_t* ri = p.rowinfo + (size_t)row * kRowInfo;
-  const int n_full = ri[0], n_tiles = ri[0] + ri[1], sa = ri[2], sb = ri[3];
-  const int ebeg = p.row_ptr[row];
-  const int n_tile_steps = n_tiles * p.cpt;
-  const int n_s1 = (sa + CK - 1) / CK;
-  const int n_steps = n_tile_steps + n_s1 + (p.S - sb + CK - 1) / CK;
-
-  const size_t head_off = (size_t)h * p.N * D;
-  const uint16_t* Qh = p.q + head_off;
-  const uint16_t* Kh = p.k + head_off;
-  const uint16_t* Vh = p.v + head_off;
-
   // Group 0 (every wave with fewer than eight) issues the HBM loads, group 1
   // (every wave with fewer than eight) transposes V.
   const bool loader = !PP || grp == 0;
   const int wl = wave, wt = PP ? wave - NW / 2 : wave;
-  const typename Stage<D, NW>::TrLane tl = Stage<D, NW>::tr_lane(lane);
+  static_assert(Stage<D, NW>::tr_split_ok(), "transpose offsets must split into wave and pass parts");
+  const typename Stage<D, NW>::TrLane tl = Stage<D, NW>::tr_lane(lane, wt);
   Stage<D, NW> stg;
   if (loader) stg.init(wl, lane, p.F);
-  // Stage 0's V^T area starts as zeros, which the first MFMA phase
-  // multiplies by P = 0. The V rows of both stages start as zeros too: a
-  // row past the sequence reads as zero, and should its LDS slot be left
-  // unwritten instead, the slot still holds a finite value (zero or an
-  // earlier row), so that P = 0 times it stays 0 in O.
-  for (int off = threadIdx.x * 16; off < Lt::VTILE; off += NW * 64 * 16)
-    *(uint4*)(buf0 + Lt::VT_OFF + off) = make_uint4(0, 0, 0, 0);
+  // The V rows of both stages start as zeros: a row past the sequence reads
+  // as zero, and should its LDS slot be left unwritten instead, the slot
+  // still holds a finite value (zero or an earlier row), so that P = 0 times
+  // it stays 0 in O.
   for (int off = threadIdx.x * 16; off < Lt::KTILE; off += NW * 64 * 16) {
     *(uint4*)(buf0 + Lt::VR_OFF + off) = make_uint4(0, 0, 0, 0);
     *(uint4*)(buf1 + Lt::VR_OFF + off) = make_uint4(0, 0, 0, 0);
   }
   __syncthreads();  // the zeros land before any load writes LDS
-  // Stage 0 holds the first step's K and V rows.
-  Cursor cur_pos;
-  cur_pos.init(p.entries + ebeg, n_tiles, n_full, n_s1, sa, sb, lane);
-  Step st_t = {0, 1, 0, 0};
-  if (n_steps > 0) {
-    st_t = cur_pos.next(p);
-    if (loader)
-#pragma unroll
-      for (int j = 0; j < Lt::LPW; ++j)
-        stg.load(Stage<D, NW>::src(p, Kh, Vh, st_t), st_t, buf0, wl, j);
-  }
 
-  // ---- Q fragments (B operand of S^T = K Q^T) and this lane's mask bounds.
-  const int q = wg_q + wave * QW + l32;
-  bf16x8 qf[D / 16];
+  // (every plan entry is checked against the buffers' bounds: a plan that
+  // is wrong cannot make the kernel read or write out of range)
+  // Work items come from this XCD's queue, in the plan's order, to
+  // whichever workgroup of the XCD asks first: the plan decides what runs
+  // and roughly when; the queue lets the workgroups that really finish
+  // first take the next item, so that neighbouring Q tiles keep running
+  // together and share their KV tiles in the L2.
+  __shared__ int s_take;
+  uint32_t xcc = __builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 20) & 0xF;  // XCC_ID
+  if ((int)xcc >= p.n_xcd) xcc = blockIdx.x % p.n_xcd;
+  const int q_begin = max(0, p.item_ptr[xcc]);
+  const int q_end = min(p.item_ptr[xcc + 1], p.max_items);
+  for (;;) {
+    __syncthreads();  // every wave has read the previous position
+    if (threadIdx.x == 0) s_take = atomicAdd(p.counters + xcc, 1);
+    __syncthreads();
+    const int it = q_begin + __builtin_amdgcn_readfirstlane(s_take);
+    if (it >= q_end) break;
+    // the item and its row: (unit, first step, end step, partial slot),
+    // (FULL tiles, executed tiles, first entry, sink a), (sink b, head,
+    // first query row, head kind)
+    const int4* idp = ARG(items) + 3 * (size_t)it;
+    const int4 item = idp[0], ib = idp[1], ic = idp[2];
+    const int n_full = ib.x, n_tiles = ib.y, ebeg = ib.z, sa = ib.w, sb = ic.x;
+    const int h = ic.y, wg_q = ic.z, kind = ic.w;
+    if (item.x < 0 || item.x >= ARG(n_units) || item.w >= ARG(max_slots) || h < 0 ||
+        h >= ARG(H) || wg_q < 0 || wg_q >= p.N || n_full < 0 || n_full > n_tiles ||
+        n_tiles > ARG(n_k_tiles) || ebeg < 0 || ebeg > ARG(entry_cap) - n_tiles || sa < 0 ||
+        sa > p.S || sb < sa || sb > p.S)
+      continue;
+    const int BQ = ARG(BQ), qt = wg_q / BQ;
+
+    const int n_tile_steps = n_tiles * p.cpt;
+    const int n_s1 = (sa + CK - 1) / CK;
+    const int n_row_steps = n_tile_steps + n_s1 + (p.S - sb + CK - 1) / CK;
+    // this item's steps (the last part of a row runs to its end)
+    const int s_first = max(0, min(item.y, n_row_steps));
+    const int n_steps = max(0, min(item.z, n_row_steps) - s_first);
+
+    const size_t head_off = (size_t)h * p.N * D;
+    const uint16_t* Qh = ARG(q) + head_off;
+    const uint16_t* Kh = p.k + head_off;
+    const uint16_t* Vh = p.v + head_off;
+
+    // Stage 0's V^T area starts as zeros, which the first MFMA phase
+    // multiplies by P = 0. (Nobody reads it now: the previous item ended with
+    // a barrier after its last LDS access, and the loads below go elsewhere.)
+    for (int off = threadIdx.x * 16; off < Lt::VTILE; off += NW * 64 * 16)
+      *(uint4*)(buf0 + Lt::VT_OFF + off) = make_uint4(0, 0, 0, 0);
+    // Stage 0 holds the first step's K and V rows.
+    Cursor cur_pos;
+    cur_pos.init(ARG(entries) + ebeg, n_tiles, n_full, n_s1, sa, sb, lane, p.cpt, s_first);
+    Step st_t = {0, 1, 0, 0};
+    if (n_steps > 0) {
+      st_t = cur_pos.next(p);
+      if (loader)
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (q < p.N) x = *(const uint4*)(Qh + (size_t)q * D + ks * 16 + hl * 8);
-    qf[ks] = __builtin_bit_cast(bf16x8, x);
-  }
-  int wlo = 0, whi = p.N, slim = 0;
-  bool msink = false;
-  if (kind == SVG_HEAD_SPATIAL) {
-    const int f = q / p.S;
-    wlo = max(0, f - p.W_f) * p.S;
-    whi = min(p.F, f + p.W_f + 1) * p.S;
-    slim = p.sink ? p.S : 0;
-  } else if (kind == SVG_HEAD_TEMPORAL) {
-    const int s = q / p.F;
-    wlo = max(0, s - p.W_s) * p.F;
-    whi = min(p.S, s + p.W_s + 1) * p.F;
-    msink = p.sink != 0;
-  }
-  if (p.round_tile && kind != SVG_HEAD_DENSE) {
-    // Tile-aligned mask: a pair is kept when its (BQ x BK) tile holds any pair
-    // of the contiguous mask part, so the bound is the same for every row of
-    // the map's Q tile: the union of its rows' windows (or bands), widened to
-    // whole KV tiles; the spatial sink [0, S) is widened the same way and the
-    // temporal strided sink stays exact.
-    const int t0 = qt * p.BQ, t1 = min(p.N, t0 + p.BQ) - 1;
+        for (int j = 0; j < Lt::LPW; ++j)
+          stg.load(Stage<D, NW>::src(p, Kh, Vh, st_t), st_t, buf0, wl, wl * 1024, j);
+    }
+
+    // ---- Q fragments (B operand of S^T = K Q^T) and this lane's mask bounds.
+    const int q = wg_q + wave * QW + l32;
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (q < p.N) x = *(const uint4*)(Qh + (size_t)q * D + ks * 16 + hl * 8);
+      qf[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+    int wlo = 0, whi = p.N, slim = 0;
+    bool msink = false;
+    const int W_f = ARG(W_f), W_s = ARG(W_s), sink = ARG(sink);
     if (kind == SVG_HEAD_SPATIAL) {
-      wlo = max(0, t0 / p.S - p.W_f) * p.S;
-      whi = min(p.F, t1 / p.S + p.W_f + 1) * p.S;
-    } else {
-      wlo = max(0, t0 / p.F - p.W_s) * p.F;
-      whi = min(p.S, t1 / p.F + p.W_s + 1) * p.F;
+      const int f = q / p.S;
+      wlo = max(0, f - W_f) * p.S;
+      whi = min(p.F, f + W_f + 1) * p.S;
+      slim = sink ? p.S : 0;
+    } else if (kind == SVG_HEAD_TEMPORAL) {
+      const int s = q / p.F;
+      wlo = max(0, s - W_s) * p.F;
+      whi = min(p.S, s + W_s + 1) * p.F;
+      msink = sink != 0;
     }
-    wlo = wlo / p.BK * p.BK;
-    whi = min(p.N, (whi + p.BK - 1) / p.BK * p.BK);
-    if (slim > 0) slim = min(p.N, (slim + p.BK - 1) / p.BK * p.BK);
-  }
-
-  f32x16 o[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
-  float m_ref = NEG_INF, l_sum = 0.f;
-  f32x16 s[2];   // S^T of a step, from its MFMA phase to its softmax phase
-  bf16x8 pf[4];  // P^T of a step, from its softmax phase to the next MFMA phase
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) pf[kk] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-
-  // Per-lane LDS read bases (the rest of every address is a constant).
-  const int k_lane = l32 * Lt::KROW + 16 * hl;
-  const int v_lane = Lt::KTILE + l32 * Lt::VTROW + 16 * hl;
-  // A operand of S^T MFMA i (d-step i/2, key block i%2): 32 keys x 16 dims.
-  auto kread = [&](const char* kb, int i) __attribute__((always_inline)) {
-    return *(const bf16x8*)(kb + (i & 1) * 32 * Lt::KROW + (i >> 1) * 32);
-  };
-  // A operand of O^T MFMA i (16-key step i/NDB, d block i%NDB): 32 dims x 16
-  // keys, 8 consecutive keys of one dim per lane.
-  auto vread = [&](const char* vb, int i) __attribute__((always_inline)) {
-    const int kk = i / NDB, db = i % NDB;
-    return *(const bf16x8*)(vb + 32 * db * Lt::VTROW + 32 * kk);
-  };
-  auto opread = [&](const char* kb, const char* vb, int i) __attribute__((always_inline)) {
-    return i < NPV ? vread(vb, i) : kread(kb, i - NPV);
-  };
-
-  // MFMA phase on the stage in `cb`: O^T += V^T P^T for the previous step,
-  // then S^T = K Q^T for this one; operands read PD MFMAs ahead. The wave is
-  // idle between its MFMAs, so other memory work rides along: side.at(i)
-  // emits it after MFMA i and side.pattern(i) places it in the schedule.
-  auto mphase = [&](const char* cb, auto&& side) __attribute__((always_inline)) {
-    const char* kb = cb + k_lane;
-    const char* vb = cb + v_lane;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[kb2][v] = 0.f;
-    bf16x8 a[PD];
-#pragma unroll
-    for (int i = 0; i < PD; ++i) a[i] = opread(kb, vb, i);
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      const bf16x8 x = a[i % PD];
-      if (i + PD < NM) a[i % PD] = opread(kb, vb, i + PD);
-      if (i < NPV) {
-        o[i % NDB] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, pf[i / NDB], o[i % NDB], 0, 0, 0);
+    if (ARG(round_tile) && kind != SVG_HEAD_DENSE) {
+      // Tile-aligned mask: a pair is kept when its (BQ x BK) tile holds any pair
+      // of the contiguous mask part, so the bound is the same for every row of
+      // the map's Q tile: the union of its rows' windows (or bands), widened to
+      // whole KV tiles; the spatial sink [0, S) is widened the same way and the
+      // temporal strided sink stays exact.
+      const int t0 = qt * BQ, t1 = min(p.N, t0 + BQ) - 1;
+      if (kind == SVG_HEAD_SPATIAL) {
+        wlo = max(0, t0 / p.S - W_f) * p.S;
+        whi = min(p.F, t1 / p.S + W_f + 1) * p.S;
       } else {
-        const int k = i - NPV;
-        s[k & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, qf[k >> 1], s[k & 1], 0, 0, 0);
+        wlo = max(0, t0 / p.F - W_s) * p.F;
+        whi = min(p.S, t1 / p.F + W_s + 1) * p.F;
       }
-      side.at(i);
+      wlo = wlo / p.BK * p.BK;
+      whi = min(p.N, (whi + p.BK - 1) / p.BK * p.BK);
+      if (slim > 0) slim = min(p.N, (slim + p.BK - 1) / p.BK * p.BK);
     }
-    // Keep the reads ahead of their MFMAs (the default schedule assumes a
-    // far shorter LDS latency).
-    __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i + PD < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      side.pattern(i);
-    }
-  };
 
-  // Softmax phase of step `cur`: mask, lazy running maximum, P^T = exp2(...)
-  // in bf16 and the row sum.
-  auto vphase = [&](const Step& cur) __attribute__((always_inline)) {
-    // mask: column limit of short steps, head predicate on boundary tiles.
-    // Key kl of the step sits at row base + kl * stride, so the window, the
-    // spatial sink and the column limit are intervals of kl and the strided
-    // sink (rows that are multiples of F) is a pattern shared by the wave:
-    // the step's 64 keep bits form one 64-bit mask per lane, of which the
-    // lane keeps the bytes of its own keys (8-key groups 2c + hl).
-    if (cur.pred) {
-      const int sd = cur.stride;
-      auto kl_at = [&](int x) __attribute__((always_inline)) {  // first key at or past row x
-        const int d = x - cur.base;
-        int k = 0;
-        if (d > 0) k = sd == 1 ? d : (d + sd - 1) / sd;
-        return min(k, 64);
-      };
-      auto ge = [](int a) __attribute__((always_inline)) {  // keys a..63
-        return a >= 64 ? 0ull : ~0ull << a;
-      };
-      uint64_t m = (ge(kl_at(wlo)) & ~ge(kl_at(whi))) | ~ge(kl_at(slim));
-      if (msink) {
-        uint64_t pat = 0;
-        if (sd == 1) {
-          for (int k = (p.F - cur.base % p.F) % p.F; k < 64; k += p.F) pat |= 1ull << k;
-        } else if (cur.base % p.F == 0) {
-          pat = ~0ull;  // a stride of F keeps the row residue mod F
-        }
-        m |= pat;
-      }
-      m &= ~ge(max(cur.ncols, 0));
-      const uint32_t keep = __builtin_amdgcn_perm((uint32_t)(m >> 32), (uint32_t)m,
-                                                  hl ? 0x07050301u : 0x06040200u);
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (!((keep >> (16 * kb2 + v)) & 1u)) s[kb2][v] = NEG_INF;
-    }
-    // P^T = exp2(S^T c - m_ref c) in bf16 and this lane's part of the row sum
-    // (plain adds: v_dot2 cannot issue while the partner wave's MFMAs run)
-    auto expo = [&]() __attribute__((always_inline)) {
-      const float mc = m_ref == NEG_INF ? 0.f : m_ref * p.c;
-      float ls[2] = {0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        uint32_t w[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int v = 8 * (kk & 1) + 2 * t;
-          const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][v], p.c, -mc));
-          const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][v + 1], p.c, -mc));
-          ls[t & 1] += e0 + e1;
-          w[t] = pack_bf16(e0, e1);
-        }
-        pf[kk] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-      }
-      return ls[0] + ls[1];
-    };
-    // The lazy reference m_ref only has to keep every value at most 2^8. A
-    // partial row sum of at most 2^8 (finite) proves that for the lane's
-    // keys, so the row maximum is needed only when some lane's sum exceeds
-    // it or no reference exists yet: then the maximum over both halves of
-    // the row is taken, O and the row sum are rescaled when it grew by more
-    // than 8 in log2 units, and the values are computed again.
-    float ls = expo();
-    if (__builtin_amdgcn_ballot_w64(!(ls <= 256.f) || m_ref == NEG_INF)) {
-      float mx = NEG_INF;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb2][v]);
-      {
-        float x0, x1;
-        halves(mx, x0, x1);
-        mx = fmaxf(x0, x1);
-      }
-      const bool need = mx > m_ref + p.thr;
-      float alpha = 1.f;
-      if (need) {
-        alpha = __builtin_amdgcn_exp2f((m_ref - mx) * p.c);
-        m_ref = mx;
-      }
-      l_sum *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-      ls = expo();
-    }
-    l_sum += ls;
-  };
-
-  if (n_steps > 0) {
-    cur_pos.refill(lane);
-    Step st_next = cur_pos.next(p);  // step 1 (rows never used when there is none)
-    wait_vmem();
-    __syncthreads();  // stage 0 and the zero V^T visible to every wave
-
-    // Iteration t works on the buffer `cb` that holds the K rows of step t,
-    // V^T of step t-1 and the V rows of step t, and fills `nb` for step t+1.
-    // Group 0 runs the MFMA phase of step t (PV of step t-1, S^T of step t)
-    // with the loads of the K and V rows of step t+1 into `nb` woven in,
-    // then the softmax of step t. Group 1 runs the softmax of step t-1, then
-    // the MFMA phase of step t with the transpose of V of step t into V^T of
-    // `nb` woven in. The softmax phases carry no memory work, and the waves
-    // of a SIMD alternate: one runs its MFMAs while the other runs its
-    // softmax. Within the iteration every LDS read is of `cb`, complete since
-    // the iteration began, and every write is to `nb`, which nobody reads
-    // until the next one, so a single barrier closes the iteration once the
-    // loads and V^T writes have landed. Iteration n_steps only finishes
-    // the last PV product (its S^T reads K rows that are not loaded and is
-    // never used). One loop per group (the group is a compile-time constant
-    // in each), so that the two phase orders are never merged.
-    auto run = [&](auto grp_c) __attribute__((always_inline)) {
-      constexpr int G = decltype(grp_c)::value;
-      Step st_prev = st_t;
-      auto iter = [&](const char* cb, char* nb, int t) __attribute__((always_inline)) {
-        const bool has_v = t < n_steps;
-        // The descriptor of step t+2 is computed off the critical path: by
-        // group 0 between the MFMAs of its MFMA phase, by group 1 with its
-        // softmax (scalar work interleaved with MFMAs would delay them).
-        cur_pos.refill(lane);
-        Step st_nn;
-        if constexpr (G == 0) {
-          // One K+V load pair every LS-th MFMA (every third when there are
-          // few). After the last step they fetch rows of the last step again
-          // into a stage nobody reads.
-          struct DmaSide {
-            const Stage<D, NW>& stg;
-            typename Stage<D, NW>::Src sr;
-            const Step& st;
-            char* nb;
-            int wl;
-            __device__ __forceinline__ void at(int i) const {
-              if (i % LS == 0 && i / LS < Lt::LPW) stg.load(sr, st, nb, wl, i / LS);
-            }
-            __device__ __forceinline__ void pattern(int i) const {
-              if (i % LS == 0 && i / LS < Lt::LPW) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-            }
-          };
-          static_assert(Lt::LPW <= NM, "every load pair needs an MFMA slot");
-          if (!PP) Stage<D, NW>::transpose(cb, nb, tl, wt);
-          st_nn = cur_pos.next(p);
-          mphase(cb, DmaSide{stg, Stage<D, NW>::src(p, Kh, Vh, st_next), st_next, nb, wl});
-          if (PP) phase_fence();
-          if (has_v) vphase(st_t);
-        } else {
-          // The transpose reads its V rows at the start of the softmax phase
-          // (the VALU-bound phase issues them almost for free) and writes V^T
-          // during the MFMA phase, long after the reads have landed, so no
-          // write waits. After the last step it fills a V^T nobody reads.
-          i16x8 trbuf[Lt::TPW];
-#pragma unroll
-          for (int j = 0; j < Lt::TPW; ++j) trbuf[j] = Stage<D, NW>::tr_read(cb, tl, wt, j);
-          st_nn = cur_pos.next(p);
-          if (t > 0) vphase(st_prev);
-          phase_fence();
-          // write j after MFMA 4j+2
-          struct TrSide {
-            char* nb;
-            const typename Stage<D, NW>::TrLane& tl;
-            int wt;
-            const i16x8 (&buf)[Lt::TPW];
-            __device__ __forceinline__ void at(int i) const {
-#pragma unroll
-              for (int j = 0; j < Lt::TPW; ++j)
-                if (i == 4 * j + 2) Stage<D, NW>::tr_write(nb, tl, wt, j, buf[j]);
-            }
-            __device__ __forceinline__ void pattern(int i) const {
-#pragma unroll
-              for (int j = 0; j < Lt::TPW; ++j)
-                if (i == 4 * j + 2) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-            }
-          };
-          static_assert(4 * Lt::TPW + 2 < NM || !PP, "transpose writes must fit the phase");
-          mphase(cb, TrSide{nb, tl, wt, trbuf});
-        }
-        // (pinned here: the scheduler would otherwise hoist the wait into
-        // the phases above)
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmem();
-        barrier_lds();
-        st_prev = st_t;
-        st_t = st_next;
-        st_next = st_nn;
-      };
-      for (int t = 0; t <= n_steps; t += 2) {
-        iter(buf0, buf1, t);
-        if (t + 1 <= n_steps) iter(buf1, buf0, t + 1);
-      }
-    };
-    if (grp == 0)
-      run(std::integral_constant<int, 0>{});
-    else
-      run(std::integral_constant<int, 1>{});
-  }
-
-  // ---- epilogue: O = O^T / l, bf16 (round to nearest even)
-  float la, lb;
-  halves(l_sum, la, lb);
-  const float lt = la + lb;
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (q < p.N) {
-    uint16_t* orow = p.o + head_off + (size_t)q * D;
+    f32x16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint2 w;
-        w.x = pack_bf16(o[db][4 * i + 0] * inv, o[db][4 * i + 1] * inv);
-        w.y = pack_bf16(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
-        *(uint2*)(orow + 32 * db + 8 * i + 4 * hl) = w;
+      for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
+    float m_ref = NEG_INF, l_sum = 0.f;
+    f32x16 s[2];   // S^T of a step, from its MFMA phase to its softmax phase
+    bf16x8 pf[4];  // P^T of a step, from its softmax phase to the next MFMA phase
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) pf[kk] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+
+    // Per-lane LDS read bases (the rest of every address is a constant).
+    const int k_lane = l32 * Lt::KROW + 16 * hl;
+    const int v_lane = Lt::KTILE + l32 * Lt::VTROW + 16 * hl;
+    // A operand of S^T MFMA i (d-step i/2, key block i%2): 32 keys x 16 dims.
+    auto kread = [&](const char* kb, int i) __attribute__((always_inline)) {
+      return *(const bf16x8*)(kb + (i & 1) * 32 * Lt::KROW + (i >> 1) * 32);
+    };
+    // A operand of O^T MFMA i (16-key step i/NDB, d block i%NDB): 32 dims x 16
+    // keys, 8 consecutive keys of one dim per lane.
+    auto vread = [&](const char* vb, int i) __attribute__((always_inline)) {
+      const int kk = i / NDB, db = i % NDB;
+      return *(const bf16x8*)(vb + 32 * db * Lt::VTROW + 32 * kk);
+    };
+    auto opread = [&](const char* kb, const char* vb, int i) __attribute__((always_inline)) {
+      return i < NPV ? vread(vb, i) : kread(kb, i - NPV);
+    };
+
+    // MFMA phase on the stage in `cb`: O^T += V^T P^T for the previous step,
+    // then S^T = K Q^T for this one; operands read PD MFMAs ahead. The wave is
+    // idle between its MFMAs, so other memory work rides along: side.at(i)
+    // emits it after MFMA i and side.pattern(i) places it in the schedule.
+    auto mphase = [&](const char* cb, auto&& side) __attribute__((always_inline)) {
+      const char* kb = cb + k_lane;
+      const char* vb = cb + v_lane;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kb2][v] = 0.f;
+      bf16x8 a[PD];
+#pragma unroll
+      for (int i = 0; i < PD; ++i) a[i] = opread(kb, vb, i);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        const bf16x8 x = a[i % PD];
+        if (i + PD < NM) a[i % PD] = opread(kb, vb, i + PD);
+        if (i < NPV) {
+          o[i % NDB] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, pf[i / NDB], o[i % NDB], 0, 0, 0);
+        } else {
+          const int k = i - NPV;
+          s[k & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, qf[k >> 1], s[k & 1], 0, 0, 0);
+        }
+        side.at(i);
       }
+      // Keep the reads ahead of their MFMAs (the default schedule assumes a
+      // far shorter LDS latency).
+      __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + PD < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        side.pattern(i);
+      }
+    };
+
+    // Softmax phase of step `cur`: mask, lazy running maximum, P^T = exp2(...)
+    // in bf16 and the row sum.
+    auto vphase = [&](const Step& cur) __attribute__((always_inline)) {
+      // mask: column limit of short steps, head predicate on boundary tiles.
+      // Key kl of the step sits at row base + kl * stride, so the window, the
+      // spatial sink and the column limit are intervals of kl and the strided
+      // sink (rows that are multiples of F) is a pattern shared by the wave:
+      // the step's 64 keep bits form one 64-bit mask per lane, of which the
+      // lane keeps the bytes of its own keys (8-key groups 2c + hl).
+      if (cur.pred) {
+        const int sd = cur.stride;
+        auto kl_at = [&](int x) __attribute__((always_inline)) {  // first key at or past row x
+          const int d = x - cur.base;
+          int k = 0;
+          if (d > 0) k = sd == 1 ? d : (d + sd - 1) / sd;
+          return min(k, 64);
+        };
+        auto ge = [](int a) __attribute__((always_inline)) {  // keys a..63
+          return a >= 64 ? 0ull : ~0ull << a;
+        };
+        uint64_t m = (ge(kl_at(wlo)) & ~ge(kl_at(whi))) | ~ge(kl_at(slim));
+        if (msink) {
+          uint64_t pat = 0;
+          if (sd == 1) {
+            for (int k = (p.F - cur.base % p.F) % p.F; k < 64; k += p.F) pat |= 1ull << k;
+          } else if (cur.base % p.F == 0) {
+            pat = ~0ull;  // a stride of F keeps the row residue mod F
+          }
+          m |= pat;
+        }
+        m &= ~ge(max(cur.ncols, 0));
+        const uint32_t keep = __builtin_amdgcn_perm((uint32_t)(m >> 32), (uint32_t)m,
+                                                    hl ? 0x07050301u : 0x06040200u);
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (!((keep >> (16 * kb2 + v)) & 1u)) s[kb2][v] = NEG_INF;
+      }
+      // P^T = exp2(S^T c - m_ref c) in bf16 and this lane's part of the row sum
+      // (plain adds: v_dot2 cannot issue while the partner wave's MFMAs run)
+      auto expo = [&]() __attribute__((always_inline)) {
+        const float mc = m_ref == NEG_INF ? 0.f : m_ref * p.c;
+        float ls[2] = {0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          uint32_t w[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int v = 8 * (kk & 1) + 2 * t;
+            const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][v], p.c, -mc));
+            const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][v + 1], p.c, -mc));
+            ls[t & 1] += e0 + e1;
+            w[t] = pack_bf16(e0, e1);
+          }
+          pf[kk] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+        return ls[0] + ls[1];
+      };
+      // The lazy reference m_ref only has to keep every value at most 2^8. A
+      // partial row sum of at most 2^8 (finite) proves that for the lane's
+      // keys, so the row maximum is needed only when some lane's sum exceeds
+      // it or no reference exists yet: then the maximum over both halves of
+      // the row is taken, O and the row sum are rescaled when it grew by more
+      // than 8 in log2 units, and the values are computed again.
+      float ls = expo();
+      if (__builtin_amdgcn_ballot_w64(!(ls <= 256.f) || m_ref == NEG_INF)) {
+        float mx = NEG_INF;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb2][v]);
+        {
+          float x0, x1;
+          halves(mx, x0, x1);
+          mx = fmaxf(x0, x1);
+        }
+        const bool need = mx > m_ref + p.thr;
+        float alpha = 1.f;
+        if (need) {
+          alpha = __builtin_amdgcn_exp2f((m_ref - mx) * p.c);
+          m_ref = mx;
+        }
+        l_sum *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+        ls = expo();
+      }
+      l_sum += ls;
+    };
+
+    if (n_steps > 0) {
+      cur_pos.refill(lane);
+      Step st_next = cur_pos.next(p);  // step 1 (rows never used when there is none)
+      wait_vmem();
+      __syncthreads();  // stage 0 and the zero V^T visible to every wave
+
+      // Iteration t works on the buffer `cb` that holds the K rows of step t,
+      // V^T of step t-1 and the V rows of step t, and fills `nb` for step t+1.
+      // Group 0 runs the MFMA phase of step t (PV of step t-1, S^T of step t)
+      // with the loads of the K and V rows of step t+1 into `nb` woven in,
+      // then the softmax of step t. Group 1 runs the softmax of step t-1, then
+      // the MFMA phase of step t with the transpose of V of step t into V^T of
+      // `nb` woven in. The softmax phases carry no memory work, and the waves
+      // of a SIMD alternate: one runs its MFMAs while the other runs its
+      // softmax. Within the iteration every LDS read is of `cb`, complete since
+      // the iteration began, and every write is to `nb`, which nobody reads
+      // until the next one, so a single barrier closes the iteration once the
+      // loads and V^T writes have landed. Iteration n_steps only finishes
+      // the last PV product (its S^T reads K rows that are not loaded and is
+      // never used). One loop per group (the group is a compile-time constant
+      // in each), so that the two phase orders are never merged.
+      auto run = [&](auto grp_c) __attribute__((always_inline)) {
+        constexpr int G = decltype(grp_c)::value;
+        Step st_prev = st_t;
+        auto iter = [&](const char* cb, char* nb, int t) __attribute__((always_inline)) {
+          const bool has_v = t < n_steps;
+          // The descriptor of step t+2 is computed off the critical path: by
+          // group 0 between the MFMAs of its MFMA phase, by group 1 with its
+          // softmax (scalar work interleaved with MFMAs would delay them).
+          cur_pos.refill(lane);
+          Step st_nn;
+          if constexpr (G == 0) {
+            // One K+V load pair every LS-th MFMA (every third when there are
+            // few). After the last step they fetch rows of the last step again
+            // into a stage nobody reads.
+            struct DmaSide {
+              const Stage<D, NW>& stg;
+              typename Stage<D, NW>::Src sr;
+              const Step& st;
+              char* nb;
+              int wl, wl1k;
+              __device__ __forceinline__ void at(int i) const {
+                if (i % LS == 0 && i / LS < Lt::LPW) stg.load(sr, st, nb, wl, wl1k, i / LS);
+              }
+              __device__ __forceinline__ void pattern(int i) const {
+                if (i % LS == 0 && i / LS < Lt::LPW)
+                  __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+              }
+            };
+            static_assert(Lt::LPW <= NM, "every load pair needs an MFMA slot");
+            if (!PP) Stage<D, NW>::transpose(cb, nb, tl);
+            st_nn = cur_pos.next(p);
+            // (laundered once per step: see Stage::load)
+            int wl1k = wl * 1024;
+            asm volatile("" : "+s"(wl1k));
+            mphase(cb,
+                   DmaSide{stg, Stage<D, NW>::src(p, Kh, Vh, st_next), st_next, nb, wl, wl1k});
+            if (PP) phase_fence();
+            if (has_v) vphase(st_t);
+          } else {
+            // The transpose reads its V rows at the start of the softmax phase
+            // (the VALU-bound phase issues them almost for free) and writes V^T
+            // during the MFMA phase, long after the reads have landed, so no
+            // write waits. After the last step it fills a V^T nobody reads.
+            i16x8 trbuf[Lt::TPW];
+#pragma unroll
+            for (int j = 0; j < Lt::TPW; ++j) trbuf[j] = Stage<D, NW>::tr_read(cb, tl, j);
+            st_nn = cur_pos.next(p);
+            if (t > 0) vphase(st_prev);
+            phase_fence();
+            // write j after MFMA 4j+2
+            struct TrSide {
+              char* nb;
+              const typename Stage<D, NW>::TrLane& tl;
+              const i16x8 (&buf)[Lt::TPW];
+              __device__ __forceinline__ void at(int i) const {
+#pragma unroll
+                for (int j = 0; j < Lt::TPW; ++j)
+                  if (i == 4 * j + 2) Stage<D, NW>::tr_write(nb, tl, j, buf[j]);
+              }
+              __device__ __forceinline__ void pattern(int i) const {
+#pragma unroll
+                for (int j = 0; j < Lt::TPW; ++j)
+                  if (i == 4 * j + 2) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+              }
+            };
+            static_assert(4 * Lt::TPW + 2 < NM || !PP, "transpose writes must fit the phase");
+            mphase(cb, TrSide{nb, tl, trbuf});
+          }
+          // (pinned here: the scheduler would otherwise hoist the wait into
+          // the phases above)
+          __builtin_amdgcn_sched_barrier(0);
+          wait_vmem();
+          barrier_lds();
+          st_prev = st_t;
+          st_t = st_next;
+          st_next = st_nn;
+        };
+        for (int t = 0; t <= n_steps; t += 2) {
+          iter(buf0, buf1, t);
+          if (t + 1 <= n_steps) iter(buf1, buf0, t + 1);
+        }
+      };
+      if (grp == 0)
+        run(std::integral_constant<int, 0>{});
+      else
+        run(std::integral_constant<int, 1>{});
+    }
+
+    // ---- epilogue. A whole row: O = O^T / l in bf16 (round to nearest even).
+    // A part of a cut row: the unnormalised O^T, the running maximum and the
+    // row sum to its partial slot, for combine_kernel.
+    float la, lb;
+    halves(l_sum, la, lb);
+    const float lt = la + lb;
+    // (the slot and the head read again, not held across the steps)
+    const int4* idq = ARG(items) + 3 * (size_t)it;
+    const int slot = __builtin_amdgcn_readfirstlane(reload_int4(idq)[3]);
+    const int h_end = __builtin_amdgcn_readfirstlane(reload_int4(idq + 2)[1]);
+    if (slot < 0) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      if (q < p.N) {
+        uint16_t* orow = ARG(o) + (size_t)h_end * p.N * D + (size_t)q * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint2 w;
+            w.x = pack_bf16(o[db][4 * i + 0] * inv, o[db][4 * i + 1] * inv);
+            w.y = pack_bf16(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
+            *(uint2*)(orow + 32 * db + 8 * i + 4 * hl) = w;
+          }
+      }
+    } else {
+      const size_t r = (size_t)slot * WGQ + wave * QW + l32;
+      float* po = ARG(part_o) + r * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *(float4*)(po + 32 * db + 8 * i + 4 * hl) =
+              make_float4(o[db][4 * i + 0], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]);
+      if (hl == 0) ARG(part_ml)[r] = make_float2(m_ref, lt);
+    }
+  }  // work items
+}
+
+// Merge the parts of cut rows: with M the largest running maximum over a
+// row's parts and w_i = 2^((m_i - M) c), O = sum_i w_i O_i / sum_i w_i l_i,
+// rounded to bf16 as the attention kernel rounds whole rows. A workgroup
+// takes one block of CRB query rows of one combine entry: it first puts each
+// row's normalised weights w_i / L in LDS, then streams the parts' O rows
+// (coalesced 16-byte loads) into per-thread sums. Entries past the plan's
+// count exit at once.
+struct CombineParams {
+  uint16_t* o;
+  const float* part_o;
+  const float2* part_ml;
+  const int32_t* header;  // [1]: combine entries
+  const int4* combine;    // (unit, first slot, parts, -)
+  int32_t N, nQ, BQ, nsub, n_units, max_slots;
+  float c;
+};
+
+constexpr int CRB = 64;   // query rows per combine workgroup
+constexpr int CPC = 16;   // parts weighted per pass
+
+template <int D, int WGQ>
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  constexpr int RB = WGQ < CRB ? WGQ : CRB;
+  constexpr int NB = WGQ / RB;         // row blocks per entry
+  constexpr int PER = RB * (D / 4) / 256;  // float4 sums per thread
+  static_assert(RB * (D / 4) % 256 == 0, "row block must split over the threads");
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  __shared__ float wts[CPC][RB];
+  const int ei = blockIdx.x / NB, rb = blockIdx.x - ei * NB;
+  if (ei >= p.header[1]) return;
+  const int4 e = p.combine[ei];
+  if (e.x < 0 || e.x >= p.n_units || e.y < 0 || e.z < 1 || e.z > p.max_slots - e.y) return;
+  const int row = e.x / p.nsub, sub = e.x - row * p.nsub;
+  const int h = row / p.nQ, qt = row - h * p.nQ;
+  const int r0 = rb * RB;                      // first row of the block within the slice
+  const int q0 = qt * p.BQ + sub * WGQ + r0;   // its query row
+  const int t = threadIdx.x;
+  // every row's largest maximum and weighted sum (thread t < RB: row t)
+  float M = NEG_INF, L = 0.f;
+  if (t < RB) {
+    for (int i = 0; i < e.z; ++i) M = fmaxf(M, p.part_ml[(size_t)(e.y + i) * WGQ + r0 + t].x);
+    for (int i = 0; i < e.z; ++i) {
+      const float2 ml = p.part_ml[(size_t)(e.y + i) * WGQ + r0 + t];
+      L += ml.x == NEG_INF ? 0.f : ml.y * __builtin_amdgcn_exp2f((ml.x - M) * p.c);
+    }
+  }
+  const float invL = L > 0.f ? 1.f / L : 0.f;
+  float4 acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = 0; i0 < e.z; i0 += CPC) {
+    const int np = min(CPC, e.z - i0);
+    __syncthreads();  // the previous pass is done with the weights
+    if (t < RB)
+      for (int i = 0; i < np; ++i) {
+        const float2 ml = p.part_ml[(size_t)(e.y + i0 + i) * WGQ + r0 + t];
+        wts[i][t] = ml.x == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((ml.x - M) * p.c) * invL;
+      }
+    __syncthreads();
+    for (int i = 0; i < np; ++i) {
+      const float* po = p.part_o + ((size_t)(e.y + i0 + i) * WGQ + r0) * D;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int idx = t + 256 * j, r = idx / (D / 4);
+        const float wgt = wts[i][r];
+        const float4 x = *(const float4*)(po + 4 * idx);
+        acc[j].x += x.x * wgt;
+        acc[j].y += x.y * wgt;
+        acc[j].z += x.z * wgt;
+        acc[j].w += x.w * wgt;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int idx = t + 256 * j, r = idx / (D / 4), c4 = idx - r * (D / 4);
+    if (q0 + r >= p.N) continue;
+    uint2 out;
+    out.x = pack_bf16(acc[j].x, acc[j].y);
+    out.y = pack_bf16(acc[j].z, acc[j].w);
+    *(uint2*)(p.o + ((size_t)h * p.N + q0 + r) * D + 4 * c4) = out;
   }
 }
 
@@ -775,23 +954,40 @@ int waves_for(int32_t tile_q) {
   return 0;
 }
 
+// Zero a launch's queue positions (a kernel rather than a memset, so that
+// the launch sequence can also be captured into a graph).
+__global__ __launch_bounds__(64) void zero_counters_kernel(int32_t* c, int32_t n) {
+  for (int i = threadIdx.x; i < n; i += 64) c[i] = 0;
+}
+
 template <int D, int NW>
-hipError_t launch(const KParams& kp, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW>), dim3(kp.total_wg), dim3(NW * 64), 0, stream, kp);
+hipError_t launch(const KParams& kp, const CombineParams& cp, int n_wg, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, stream, kp.counters, kp.n_xcd);
+  hipError_t e0 = hipGetLastError();
+  if (e0 != hipSuccess) return e0;
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW>), dim3(n_wg), dim3(NW * 64), 0, stream, kp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int RB = NW * QW < CRB ? NW * QW : CRB;
+  hipLaunchKernelGGL((combine_kernel<D, NW * QW>), dim3(n_wg * (NW * QW / RB)), dim3(256), 0,
+                     stream, cp);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(int nw, const KParams& kp, hipStream_t stream) {
+hipError_t launch_d(int nw, const KParams& kp, const CombineParams& cp, int n_wg,
+                    hipStream_t stream) {
   switch (nw) {
-    case 8: return launch<D, 8>(kp, stream);
-    case 4: return launch<D, 4>(kp, stream);
-    case 2: return launch<D, 2>(kp, stream);
-    default: return launch<D, 1>(kp, stream);
+    case 8: return launch<D, 8>(kp, cp, n_wg, stream);
+    case 4: return launch<D, 4>(kp, cp, n_wg, stream);
+    case 2: return launch<D, 2>(kp, cp, n_wg, stream);
+    default: return launch<D, 1>(kp, cp, n_wg, stream);
   }
 }
 
 }  // namespace
+
+int32_t attn_waves(int32_t tile_q) { return waves_for(tile_q); }
 
 bool attn_supported(int32_t head_dim, int32_t tile_q, int32_t tile_k) {
   if (head_dim != 64 && head_dim != 128) return false;
@@ -799,9 +995,9 @@ bool attn_supported(int32_t head_dim, int32_t tile_q, int32_t tile_k) {
   return tile_k >= 32 && tile_k <= 1024 && tile_k % 32 == 0;
 }
 
-hipError_t launch_attn_fwd(const MapGeometry& g, const MapBuffers& b, const AttnArgs& a,
-                           hipStream_t stream) {
-  if (!attn_supported(a.head_dim, g.BQ, g.BK)) return hipErrorInvalidValue;
+hipError_t launch_attn_fwd(const MapGeometry& g, const MapBuffers& b, const PlanBuffers& pl,
+                           uint32_t ring, const AttnArgs& a, hipStream_t stream) {
+  if (!attn_supported(a.head_dim, g.BQ, g.BK) || pl.n_wg <= 0) return hipErrorInvalidValue;
   const int nw = waves_for(g.BQ);
   const int wgq = nw * QW;
   KParams kp;
@@ -820,19 +1016,38 @@ hipError_t launch_attn_fwd(const MapGeometry& g, const MapBuffers& b, const Attn
   kp.nQ = g.nQ;
   kp.nsub = g.BQ / wgq;
   kp.cpt = (g.BK + CK - 1) / CK;
-  const int64_t total = (int64_t)g.H * g.nQ * kp.nsub;
-  if (total > INT32_MAX) return hipErrorInvalidConfiguration;
-  kp.total_wg = (int32_t)total;
-  kp.kinds = b.kinds;
-  kp.rowinfo = b.rowinfo;
-  kp.row_ptr = b.row_ptr;
   kp.entries = b.entries;
+  kp.item_ptr = pl.dev + 4;
+  kp.counters = pl.counters + (size_t)(ring % kQueueRing) * pl.n_xcd;
+  kp.n_xcd = pl.n_xcd;
+  kp.items = (const int4*)(pl.dev + pl.items_off());
+  kp.H = g.H;
+  kp.n_units = (int32_t)((int64_t)g.H * g.nQ * kp.nsub);
+  kp.n_k_tiles = g.nK;
+  kp.entry_cap = (int32_t)b.capacity;
+  kp.max_items = (int32_t)pl.max_items;
+  kp.max_slots = (int32_t)pl.max_slots;
+  kp.part_o = pl.part_o;
+  kp.part_ml = (float2*)pl.part_ml;
   kp.c = a.scale * 1.4426950408889634f;
   kp.thr = 8.0f / kp.c;
   kp.mask_all = (a.flags & SVG_ATTN_MASK_ALL_TILES) ? 1 : 0;
   kp.round_tile = g.round == SVG_ROUND_TILE ? 1 : 0;
-  if (kp.total_wg <= 0) return hipSuccess;
-  return a.head_dim == 128 ? launch_d<128>(nw, kp, stream) : launch_d<64>(nw, kp, stream);
+  CombineParams cp;
+  cp.o = kp.o;
+  cp.part_o = pl.part_o;
+  cp.part_ml = (const float2*)pl.part_ml;
+  cp.header = pl.dev;
+  cp.combine = (const int4*)(pl.dev + pl.combine_off());
+  cp.N = kp.N;
+  cp.nQ = g.nQ;
+  cp.BQ = g.BQ;
+  cp.nsub = kp.nsub;
+  cp.n_units = kp.n_units;
+  cp.max_slots = kp.max_slots;
+  cp.c = kp.c;
+  return a.head_dim == 128 ? launch_d<128>(nw, kp, cp, pl.n_wg, stream)
+                           : launch_d<64>(nw, kp, cp, pl.n_wg, stream);
 }
 
 }  // namespace svg

@@ -12,6 +12,7 @@
 #include <string>
 #include <vector>
 
+#include "plan.hpp"
 #include "svg_internal.hpp"
 
 namespace {
@@ -49,6 +50,115 @@ void free_buffers(svg::MapBuffers& b) {
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   b = svg::MapBuffers{};
+}
+
+void free_plan(svg_tile_map* m) {
+  void* dev[] = {m->plan.dev, m->plan.counters, m->plan.part_o, m->plan.part_ml};
+  for (void* p : dev)
+    if (p) (void)hipFree(p);
+  if (m->job.rowinfo_host) (void)hipHostFree(m->job.rowinfo_host);
+  if (m->job.image_host) (void)hipHostFree(m->job.image_host);
+  m->plan = svg::PlanBuffers{};
+  m->job.rowinfo_host = m->job.image_host = nullptr;
+}
+
+// Everything a map owns; the caller has waited for its queued work.
+void free_map(svg_tile_map* m) {
+  if (m->built) (void)hipEventDestroy(m->built);
+  free_plan(m);
+  free_buffers(m->buf);
+  delete m;
+}
+
+// Step count of every work unit (a workgroup's slice of a schedule row, -1
+// for a slice past the end of the sequence) from the map's row info.
+void unit_steps(const PlanJob& j, std::vector<int32_t>& steps) {
+  const svg::MapGeometry& g = j.geom;
+  const int64_t R = (int64_t)g.H * g.nQ;
+  const int32_t ck = svg::kAttnStepKeys, cpt = (g.BK + ck - 1) / ck;
+  steps.resize(R * j.nsub);
+  for (int64_t r = 0; r < R; ++r) {
+    const int32_t* ri = j.rowinfo_host + r * svg::kRowInfo;
+    const int64_t n = (int64_t)(ri[0] + ri[1]) * cpt + (ri[2] + ck - 1) / ck +
+                      (g.S - ri[3] + ck - 1) / ck;
+    const int64_t q0 = (r % g.nQ) * (int64_t)g.BQ;
+    for (int32_t sub = 0; sub < j.nsub; ++sub)
+      steps[r * j.nsub + sub] = q0 + (int64_t)sub * j.wgq < g.N ? (int32_t)n : -1;
+  }
+}
+
+// Host function queued on the build stream once the row info has reached
+// the pinned staging: plans the persistent launch and writes the plan image
+// that the stream copies to the device next. It makes no HIP call. Should
+// planning fail (host memory), every unit becomes one whole item of
+// workgroup (unit mod workgroups), written without allocating.
+void plan_host_fn(void* user) {
+  PlanJob& j = *static_cast<PlanJob*>(user);
+  svg::PlanBuffers& pl = *j.plan;
+  const svg::MapGeometry& g = j.geom;
+  int32_t* im = j.image_host;
+  int32_t* ptr = im + 4;
+  svg::ItemDesc* items = reinterpret_cast<svg::ItemDesc*>(im + pl.items_off());
+  int32_t* comb = im + pl.combine_off();
+  // Each row's first schedule entry, as the device's exclusive scan places
+  // it, into the row info's unused field 6 (staging only; the device copy
+  // is not touched).
+  const int64_t R = (int64_t)g.H * g.nQ;
+  {
+    int64_t acc = 0;
+    for (int64_t r = 0; r < R; ++r) {
+      int32_t* ri = j.rowinfo_host + r * svg::kRowInfo;
+      ri[6] = (int32_t)acc;
+      acc += ri[0] + ri[1];
+    }
+  }
+  auto desc = [&](int32_t unit, int32_t s0, int32_t s1, int32_t slot) {
+    const int32_t row = unit / j.nsub, sub = unit - row * j.nsub;
+    const int32_t* ri = j.rowinfo_host + (int64_t)row * svg::kRowInfo;
+    const int32_t h = row / g.nQ, qt = row - h * g.nQ;
+    return svg::ItemDesc{unit,  s0,    s1, slot, ri[0], ri[0] + ri[1], ri[6], ri[2],
+                         ri[3], h, qt * g.BQ + sub * j.wgq, j.kinds[h]};
+  };
+  try {
+    std::vector<int32_t> steps;
+    unit_steps(j, steps);
+    std::vector<float> weight(steps.size());
+    for (size_t u = 0; u < steps.size(); ++u)
+      weight[u] = svg::kPlanStepWeight[j.kinds[(u / j.nsub) / g.nQ]];
+    svg::PlanResult r;
+    svg::plan_persistent(steps.data(), weight.data(), (int32_t)steps.size(), pl.n_wg, pl.n_xcd,
+                         svg::kPlanBlockUnits, svg::kPlanItemOverhead, svg::kPlanMinPart, r);
+    im[0] = (int32_t)r.items.size();
+    im[1] = (int32_t)r.combine.size();
+    im[2] = r.n_slots;
+    im[3] = 0;
+    std::memcpy(ptr, r.queue_ptr.data(), r.queue_ptr.size() * sizeof(int32_t));
+    for (size_t i = 0; i < r.queue_items.size(); ++i) {
+      const svg::PlanItem& it = r.queue_items[i];
+      items[i] = desc(it.unit, it.s0, it.s1, it.slot);
+    }
+    std::memcpy(comb, r.combine.data(), r.combine.size() * sizeof(svg::PlanCombine));
+    j.items = (int64_t)r.items.size();
+    j.split_units = (int64_t)r.combine.size();
+    j.slots = r.n_slots;
+    j.max_load = r.max_load;
+    j.total_load = r.total_load;
+  } catch (...) {
+    // every unit whole, in order, XCD x taking units x, x + n_xcd, ...
+    const int64_t n_units = R * j.nsub;
+    int32_t n = 0;
+    for (int32_t x = 0; x < pl.n_xcd; ++x) {
+      ptr[x] = n;
+      for (int64_t u = x; u < n_units; u += pl.n_xcd)
+        if (((u / j.nsub) % g.nQ) * (int64_t)g.BQ + (u % j.nsub) * (int64_t)j.wgq < g.N)
+          items[n++] = desc((int32_t)u, 0, svg::kPlanToEnd, -1);
+    }
+    ptr[pl.n_xcd] = n;
+    im[0] = n;
+    im[1] = im[2] = im[3] = 0;
+    j.items = n;
+    j.split_units = j.slots = j.max_load = j.total_load = 0;
+  }
 }
 
 template <typename T>
@@ -153,38 +263,100 @@ svg_status svg_build_tile_map(const svg_mask_spec* spec, int32_t tile_q, int32_t
     return fail(SVG_ERR_UNSUPPORTED, "schedule of %lld entries exceeds int32 indexing",
                 (long long)b.capacity);
   }
-  if ((e = alloc(&b.kinds, g.H)) != hipSuccess || (e = alloc(&b.classes, R * g.nK)) != hipSuccess ||
-      (e = alloc(&b.rowinfo, R * svg::kRowInfo)) != hipSuccess ||
-      (e = alloc(&b.row_ptr, R + 1)) != hipSuccess ||
-      (e = alloc(&b.entries, b.capacity)) != hipSuccess ||
-      (e = alloc(&b.rowstats, R * svg::kRowStats)) != hipSuccess ||
-      (e = alloc(&b.stats, (int64_t)g.H * svg::kRowStats)) != hipSuccess) {
-    free_buffers(b);
-    delete m;
-    return fail(e == hipErrorOutOfMemory ? SVG_ERR_OOM : SVG_ERR_HIP,
-                "device allocation for the tile map failed: %s", hipGetErrorString(e));
+  // The persistent launch: one workgroup per compute unit, workgroup i on
+  // XCD i mod (XCD count).
+  svg::PlanBuffers& pl = m->plan;
+  PlanJob& job = m->job;
+  job.geom = g;
+  job.kinds = m->kinds.data();
+  job.wgq = svg::attn_waves(tile_q) * svg::kAttnQRowsPerWave;
+  job.nsub = tile_q / job.wgq;
+  job.plan = &pl;
+  {
+    int cus = 0, xcds = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, m->device);
+    if (e == hipSuccess && hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs,
+                                                 m->device) != hipSuccess)
+      xcds = 1;
+    if (e != hipSuccess || cus < 1) {
+      delete m;
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidDevice, "compute unit count");
+    }
+    pl.n_wg = cus;
+    pl.n_xcd = xcds >= 1 && xcds <= cus ? xcds : 1;
   }
-  if ((e = hipEventCreateWithFlags(&m->built, hipEventDisableTiming)) != hipSuccess) {
-    free_buffers(b);
+  const int64_t n_units = R * job.nsub;
+  if (svg::plan_max_items(n_units, pl.n_wg) > INT32_MAX / 4) {
     delete m;
+    return fail(SVG_ERR_UNSUPPORTED, "%lld work units exceed the launch plan's indexing",
+                (long long)n_units);
+  }
+  pl.max_items = svg::plan_max_items(n_units, pl.n_wg);
+  pl.max_slots = svg::plan_max_slots(pl.n_wg);
+  const int64_t part_rows = pl.max_slots * job.wgq;
+  hipError_t ea = hipSuccess;
+  auto step = [&](hipError_t x) { if (ea == hipSuccess) ea = x; };
+  step(alloc(&b.kinds, g.H));
+  step(alloc(&b.classes, R * g.nK));
+  step(alloc(&b.rowinfo, R * svg::kRowInfo));
+  step(alloc(&b.row_ptr, R + 1));
+  step(alloc(&b.entries, b.capacity));
+  step(alloc(&b.rowstats, R * svg::kRowStats));
+  step(alloc(&b.stats, (int64_t)g.H * svg::kRowStats));
+  step(alloc(&pl.dev, pl.dev_ints()));
+  step(alloc(&pl.counters, (int64_t)svg::kQueueRing * pl.n_xcd));
+  step(alloc(&pl.part_o, part_rows * svg::kAttnMaxHeadDim));
+  step(alloc(&pl.part_ml, part_rows * 2));
+  if (ea == hipSuccess)
+    ea = hipHostMalloc(reinterpret_cast<void**>(&job.rowinfo_host),
+                       (size_t)R * svg::kRowInfo * sizeof(int32_t), hipHostMallocDefault);
+  if (ea == hipSuccess)
+    ea = hipHostMalloc(reinterpret_cast<void**>(&job.image_host),
+                       (size_t)pl.dev_ints() * sizeof(int32_t), hipHostMallocDefault);
+  if (ea != hipSuccess) {
+    free_map(m);
+    return fail(ea == hipErrorOutOfMemory ? SVG_ERR_OOM : SVG_ERR_HIP,
+                "allocation for the tile map failed: %s", hipGetErrorString(ea));
+  }
+  // An all-zero image is a valid empty plan (no items, no combine entries).
+  std::memset(job.image_host, 0, (size_t)pl.dev_ints() * sizeof(int32_t));
+  if ((e = hipEventCreateWithFlags(&m->built, hipEventDisableTiming)) != hipSuccess) {
+    m->built = nullptr;
+    free_map(m);
     return hip_fail(e, "hipEventCreate");
   }
+  // Queued on the caller's stream, nothing waited for: head kinds from
+  // kernel arguments, the tile-map kernels, the row info to the pinned
+  // staging, the planning host function, the plan image to the device.
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  e = hipMemcpyAsync(b.kinds, m->kinds.data(), sizeof(int32_t) * g.H, hipMemcpyHostToDevice, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);  // the host array may go away
-  if (e != hipSuccess) {
-    (void)hipEventDestroy(m->built);
-    free_buffers(b);
-    delete m;
-    return hip_fail(e, "copy of head kinds");
+  const char* what = "copy of head kinds";
+  e = svg::launch_set_kinds(m->kinds.data(), g.H, b.kinds, st);
+  if (e == hipSuccess) {
+    what = "tile-map kernels";
+    e = svg::launch_build_tile_map(g, b, st);
   }
-  const svg_status s = run_build(m, st);
-  if (s != SVG_OK) {
+  if (e == hipSuccess) {
+    what = "copy of row info";
+    e = hipMemcpyAsync(job.rowinfo_host, b.rowinfo, (size_t)R * svg::kRowInfo * sizeof(int32_t),
+                       hipMemcpyDeviceToHost, st);
+  }
+  if (e == hipSuccess) {
+    what = "launch planning";
+    e = hipLaunchHostFunc(st, plan_host_fn, &job);
+  }
+  if (e == hipSuccess) {
+    what = "copy of the launch plan";
+    e = hipMemcpyAsync(pl.dev, job.image_host, (size_t)pl.dev_ints() * sizeof(int32_t),
+                       hipMemcpyHostToDevice, st);
+  }
+  if (e == hipSuccess) {
+    what = "hipEventRecord";
+    e = hipEventRecord(m->built, st);
+  }
+  if (e != hipSuccess) {
     (void)hipStreamSynchronize(st);
-    (void)hipEventDestroy(m->built);
-    free_buffers(b);
-    delete m;
-    return s;
+    free_map(m);
+    return hip_fail(e, what);
   }
   *out = m;
   return ok();
@@ -279,12 +451,24 @@ svg_status svg_tile_map_copy_schedule(const svg_tile_map* map, int32_t* row_ptr,
   return ok();
 }
 
+svg_status svg_tile_map_plan_info(const svg_tile_map* map, svg_plan_info* out) {
+  if (!map || !out) return fail(SVG_ERR_INVALID_ARG, "map or out is NULL");
+  svg_status s = wait_built(map);
+  if (s != SVG_OK) return s;
+  out->workgroups = map->plan.n_wg;
+  out->xcds = map->plan.n_xcd;
+  out->work_items = map->job.items;
+  out->split_rows = map->job.split_units;
+  out->partial_slots = map->job.slots;
+  out->max_load = map->job.max_load;
+  out->total_load = map->job.total_load;
+  return ok();
+}
+
 svg_status svg_tile_map_destroy(svg_tile_map* map) {
   if (!map) return ok();
   svg_status s = wait_built(map);
-  if (map->built) (void)hipEventDestroy(map->built);
-  free_buffers(map->buf);
-  delete map;
+  free_map(map);
   return s == SVG_OK ? ok() : s;
 }
 
@@ -327,7 +511,9 @@ svg_status svg_attn_fwd(const void* q, const void* k, const void* v, void* o, in
   const svg_status ds = check_device(map);
   if (ds != SVG_OK) return ds;
   svg::AttnArgs a{q, k, v, o, head_dim, scale, flags};
-  const hipError_t e = svg::launch_attn_fwd(g, map->buf, a, reinterpret_cast<hipStream_t>(stream));
+  const uint32_t ring = map->launches.fetch_add(1, std::memory_order_relaxed) % svg::kQueueRing;
+  const hipError_t e = svg::launch_attn_fwd(g, map->buf, map->plan, ring, a,
+                                            reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   return ok();
 }
@@ -458,6 +644,11 @@ svg_status svg_route_heads(const svg_mask_spec* spec, const void* q, const void*
   if (!aligned16(q) || !aligned16(k) || !aligned16(v))
     return fail(SVG_ERR_ALIGNMENT, "q, k and v must be 16-byte aligned");
   const int32_t H = spec->num_heads;
+  // Windows wider than the sequence behave like the sequence (as in
+  // svg_build_tile_map); clamping keeps the kernels' interval arithmetic in
+  // 32-bit range.
+  const int32_t W_f = spec->frame_window < spec->frames ? spec->frame_window : spec->frames;
+  const int32_t W_s = spec->temporal_band < S ? spec->temporal_band : (int32_t)S;
   const svg::RouteLayout L = svg::route_layout(N, H, head_dim, n_rows, svg::route_slots(head_dim));
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* scratch = nullptr;
@@ -468,7 +659,7 @@ svg_status svg_route_heads(const svg_mask_spec* spec, const void* q, const void*
   e = hipMemcpyAsync(scratch + L.rows_off, rows, (size_t)n_rows * 4, hipMemcpyHostToDevice, st);
   if (e == hipSuccess)
     e = svg::launch_route(q, k, v, scratch, L, N, spec->frames, (int32_t)S, H, head_dim,
-                          spec->frame_window, spec->temporal_band, spec->sink_first_frame ? 1 : 0,
+                          W_f, W_s, spec->sink_first_frame ? 1 : 0,
                           scale, n_rows, st);
   if (e == hipSuccess)
     e = hipMemcpyAsync(err_h.data(), scratch + L.err_off, err_h.size() * 4,

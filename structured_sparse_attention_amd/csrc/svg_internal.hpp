@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <vector>
 
 #include "svg_attn.h"
@@ -35,6 +36,11 @@ struct MapBuffers {
   int64_t capacity = 0;
 };
 
+// Write the head kinds (host array [H], values 0..2) to device memory from
+// kernel arguments: queued on `stream`, the host array may go away at once.
+hipError_t launch_set_kinds(const int32_t* host_kinds, int32_t H, int32_t* dev_kinds,
+                            hipStream_t stream);
+
 // Launch the tile-map kernels (classify, scan, compact, per-head stats).
 hipError_t launch_build_tile_map(const MapGeometry& g, const MapBuffers& b,
                                  hipStream_t stream);
@@ -49,10 +55,58 @@ struct AttnArgs {
   uint32_t flags;
 };
 
-// Launch the attention forward kernel for a built map. Returns
-// hipErrorInvalidValue for a head_dim / tile size without an instance.
-hipError_t launch_attn_fwd(const MapGeometry& g, const MapBuffers& b,
-                           const AttnArgs& a, hipStream_t stream);
+// A work item as the attention kernel reads it: the plan's entry and the
+// schedule row data of its unit, so that starting an item takes one load.
+struct ItemDesc {
+  int32_t unit, s0, s1, slot;        // PlanItem
+  int32_t n_full, n_tiles, ebeg, sa;  // the row's FULL and executed tiles, its
+  int32_t sb, head, q0, kind;         //   first entry, sink range; head, first
+};                                    //   query row, head kind
+static_assert(sizeof(ItemDesc) == 48, "three 16-byte loads");
+
+// Work plan of the persistent attention launch (plan.hpp), device side.
+// `dev` holds, as int32: a header [n_items, n_combine, n_slots, 0], then
+// the per-XCD queue bounds queue_ptr [n_xcd + 1] in a field of n_wg + 1
+// entries padded to a multiple of 4, then max_items ItemDesc (12 int32
+// each, XCD by XCD in queue order) and n_wg combine entries (PlanCombine,
+// 4 int32 each). `counters` is a ring of kQueueRing sets of n_xcd queue
+// positions; every launch takes the next set and zeroes it first.
+constexpr int32_t kQueueRing = 256;
+struct PlanBuffers {
+  int32_t* dev = nullptr;
+  int32_t* counters = nullptr;  // [kQueueRing][n_xcd]
+  float* part_o = nullptr;  // [max_slots][rows of a workgroup][128]
+  float* part_ml = nullptr; // [max_slots][rows of a workgroup][2]
+  int32_t n_wg = 0, n_xcd = 0;
+  int64_t max_items = 0, max_slots = 0;
+  int64_t ptr_ints() const { return (n_wg + 1 + 3) / 4 * 4; }
+  int64_t items_off() const { return 4 + ptr_ints(); }
+  int64_t combine_off() const { return items_off() + 12 * max_items; }
+  int64_t dev_ints() const { return combine_off() + 4 * (int64_t)n_wg; }
+};
+
+// Query rows per workgroup (32 per wave) of the attention kernel for a Q
+// tile size, and its waves; 0 when the size has no kernel.
+int32_t attn_waves(int32_t tile_q);
+constexpr int32_t kAttnQRowsPerWave = 32;
+constexpr int32_t kAttnStepKeys = 64;   // keys per pipeline step
+constexpr int32_t kAttnMaxHeadDim = 128;
+// Cost of starting a work item, in steps (Q loads, stage-0 latency, epilogue).
+constexpr int32_t kPlanItemOverhead = 4;
+// Parts of a cut row are kept at least this many steps where possible.
+constexpr int32_t kPlanMinPart = 32;
+// Work units per block dealt to the XCDs in rounds (plan_persistent).
+constexpr int32_t kPlanBlockUnits = 32;
+// Relative cost of a 64-key step by head kind (spatial, temporal, dense),
+// measured on the main workload's shape with the same kernel.
+constexpr float kPlanStepWeight[3] = {1.030f, 1.000f, 0.985f};
+
+// Launch the attention forward kernel for a built map and planned launch
+// (queue positions from counter set `ring`, zeroed first), then the pass
+// that merges the parts of cut rows. Returns hipErrorInvalidValue for a
+// head_dim / tile size without an instance.
+hipError_t launch_attn_fwd(const MapGeometry& g, const MapBuffers& b, const PlanBuffers& pl,
+                           uint32_t ring, const AttnArgs& a, hipStream_t stream);
 bool attn_supported(int32_t head_dim, int32_t tile_q, int32_t tile_k);
 
 // Scratch of one routing call (byte offsets into one allocation).
@@ -82,11 +136,27 @@ hipError_t launch_permute_tokens(const void* src, void* dst, int32_t F,
 
 }  // namespace svg
 
+// Host side of the launch plan: pinned staging for the map's row info (in)
+// and the plan image (out), filled by a host function queued on the build
+// stream; the plan's statistics once it has run.
+struct PlanJob {
+  svg::MapGeometry geom;
+  int32_t nsub = 1, wgq = 256;
+  const int32_t* kinds = nullptr;   // the map's head kinds [H]
+  int32_t* rowinfo_host = nullptr;  // pinned [H*nQ][kRowInfo]
+  int32_t* image_host = nullptr;    // pinned, PlanBuffers::dev_ints()
+  svg::PlanBuffers* plan = nullptr;
+  int64_t items = 0, split_units = 0, slots = 0, max_load = 0, total_load = 0;
+};
+
 // The opaque map type of the public header.
 struct svg_tile_map {
   svg::MapGeometry geom;
   svg::MapBuffers buf;
+  svg::PlanBuffers plan;
+  PlanJob job;
   std::vector<int32_t> kinds;
   int device = 0;
   hipEvent_t built = nullptr;  // recorded after every (re)build
+  mutable std::atomic<uint32_t> launches{0};  // picks each launch's queue counters
 };

@@ -27,9 +27,10 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// 32-bit counting: sequences are at most 2^30 tokens and a tile holds at most
-// 512 x 1024 pairs, so every per-tile quantity fits; only the sums over a
-// row of tiles need 64 bits.
+// 32-bit counting: sequences are at most 2^30 tokens, and a tile holds at
+// most BQ x BK <= 2^20 x 2^10 = 2^30 pairs (the host caps both tile sizes),
+// so every per-tile quantity fits; only the sums over a row of tiles need 64
+// bits.
 __device__ __forceinline__ int span32(int a, int b) { return b > a ? b - a : 0; }
 // min(lim, v + w + 1) without forming v + w + 1 (w may be near INT32_MAX)
 __device__ __forceinline__ int upper(int v, int w, int lim) { return w >= lim - v ? lim : v + w + 1; }
@@ -228,6 +229,17 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(MapGeometry g, MapBuf
   }
 }
 
+// Head kinds of up to kKindChunk heads, carried in the kernel arguments so
+// that the build needs neither a host-to-device copy nor a wait for one.
+constexpr int kKindChunk = 256;
+struct KindChunk {
+  int32_t h0, n;
+  int8_t kind[kKindChunk];
+};
+__global__ __launch_bounds__(kKindChunk) void set_kinds_kernel(KindChunk c, int32_t* kinds) {
+  if ((int)threadIdx.x < c.n) kinds[c.h0 + threadIdx.x] = c.kind[threadIdx.x];
+}
+
 __global__ __launch_bounds__(kThreads) void stats_kernel(MapGeometry g, MapBuffers b) {
   const int h = blockIdx.x;
   int64_t acc[kRowStats] = {};
@@ -245,6 +257,20 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(MapGeometry g, MapBuffe
 }
 
 }  // namespace
+
+hipError_t launch_set_kinds(const int32_t* host_kinds, int32_t H, int32_t* dev_kinds,
+                            hipStream_t stream) {
+  for (int32_t h0 = 0; h0 < H; h0 += kKindChunk) {
+    KindChunk c;
+    c.h0 = h0;
+    c.n = H - h0 < kKindChunk ? H - h0 : kKindChunk;
+    for (int i = 0; i < kKindChunk; ++i) c.kind[i] = (int8_t)(i < c.n ? host_kinds[h0 + i] : 0);
+    hipLaunchKernelGGL(set_kinds_kernel, dim3(1), dim3(kKindChunk), 0, stream, c, dev_kinds);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_build_tile_map(const MapGeometry& g, const MapBuffers& b,
                                  hipStream_t stream) {

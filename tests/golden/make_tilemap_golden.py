@@ -38,6 +38,12 @@ def cases():
     ta = si.workload("tile-aligned")
     for bq, bk in si.SWEEP_TILES:
         out.append(ta.with_tiles(bq, bk))
+    # the exact masks of the main workload at every swept tile pair (the
+    # pair the tile search picks is the one a caller runs)
+    main = si.workload("main")
+    for bq, bk in si.SWEEP_TILES:
+        if (bq, bk) != (main.tile_q, main.tile_k):
+            out.append(main.with_tiles(bq, bk))
     return out
 
 

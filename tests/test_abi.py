@@ -191,3 +191,30 @@ def _load_fresh(path):
         return _lib.load(path)
     finally:
         _lib._lib = saved
+
+
+class _FakeDeviceTensor:
+    """Stands in for a CUDA bf16 tensor: the wrappers' checks run before any
+    pointer reaches the library, so nothing is dereferenced."""
+
+    def __init__(self, shape):
+        import torch
+        self.shape = shape
+        self.dtype = torch.bfloat16
+        self.is_cuda = True
+
+    def is_contiguous(self):
+        return True
+
+    def data_ptr(self):
+        return 1 << 20
+
+
+def test_wrappers_reject_a_head_kind_list_of_the_wrong_length():
+    t = _FakeDeviceTensor((2, 256, 64))
+    with pytest.raises(ValueError, match="head_kind has 1 entries"):
+        svg.svg_attn_fwd(t, t, t, t, ["spatial"], None)
+    with pytest.raises(ValueError, match="head_kind has 3 entries"):
+        svg.svg_attn_fwd(t, t, t, t, ["spatial", "temporal", "dense"], None)
+    with pytest.raises(ValueError, match="head_kind has 1 entries"):
+        svg.svg_permute_tokens(t, t, 4, 64, ["temporal"], svg.TO_KERNEL_LAYOUT)

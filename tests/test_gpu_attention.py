@@ -24,7 +24,7 @@ import structured_sparse_attention_amd as svg
 from gpu_harness import (build_map, from_device, run_attention, say, to_device,
                          to_kernel_layout, to_original_layout)
 from oracle_cases import masks_of, params_of, widen
-from oracle_pool import oracle_rows
+from oracle_pool import compare_all_rows, oracle_rows
 from test_oracle_pins import RAGGED, RAGGED_NOSINK
 
 pytestmark = pytest.mark.gpu
@@ -73,7 +73,18 @@ SMALL = [si.workload("tiny"), si.workload("tiny-misaligned"), RAGGED, RAGGED_NOS
          si.Workload("d128-bq32", 5, 9, 10, ("spatial", "temporal", "dense"), 128, 1, 13, True,
                      32, 64, False, seed=38),
          si.Workload("d128-bq64", 4, 7, 11, ("spatial", "temporal"), 128, 1, 9, True,
-                     64, 32, False, seed=39)]
+                     64, 32, False, seed=39),
+         # the 8-wave kernel with one step per KV tile (the tile search's
+         # choice on the main workload), exact masks, ragged tails
+         si.Workload("d128-bk64", 5, 9, 10, ("spatial", "temporal", "dense"), 128, 1, 13, True,
+                     256, 64, False, seed=40),
+         # rows long enough for the launch plan to cut them between
+         # workgroups: their parts go through partial results and the
+         # combine pass (ragged: 4,185 tokens)
+         si.Workload("d128-split", 5, 27, 31, ("dense", "spatial", "temporal"), 128, 1, 60,
+                     True, 256, 64, False, seed=46),
+         si.Workload("d64-split-bq32", 5, 27, 31, ("spatial", "temporal"), 64, 1, 60, True,
+                     32, 64, False, seed=47)]
 # the tile-aligned mask on the degenerate shapes: zero windows without the
 # sink, windows wider than the sequence, a single frame
 SMALL += [_aligned(w) for w in SMALL if w.name in ("narrow", "wide", "one-frame")]
@@ -142,6 +153,64 @@ def test_full_size_sampled_rows(name):
     rows = _sample_rows(w, 192)
     ref = oracle_rows(w, Q, K, V, masks_of(w), rows)
     check(o[:, rows], ref, name)
+
+
+@pytest.mark.parametrize("name", ["d128-split", "d64-split-bq32"])
+def test_launch_plan_cuts_rows_of_the_split_shapes(name):
+    # the shapes above exist to exercise cut rows: make sure the plan cuts
+    w = {x.name: x for x in SMALL}[name]
+    tm = build_map(w)
+    info = tm.plan_info()
+    tm.destroy()
+    say(f"[plan] {w.name}: {info}")
+    assert info["split_rows"] > 0 and info["partial_slots"] >= 2 * info["split_rows"]
+
+
+def test_main_launch_plan_is_level():
+    w = si.workload("main")
+    tm = build_map(w)
+    info = tm.plan_info()
+    tm.destroy()
+    mean = info["total_load"] / info["workgroups"]
+    say(f"[plan] main: {info}, busiest / mean = {info['max_load'] / mean:.4f}")
+    assert info["max_load"] / mean < 1.01
+    assert info["partial_slots"] <= 2 * info["workgroups"]
+
+
+# Every output row of the main, dense and tile-aligned (256 x 128) workloads
+# against the oracle. The oracle runs in a process pool; the comparison is
+# made in the workers.
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["main", "dense", "tile-aligned"])
+def test_full_size_every_row(name):
+    import time
+    w = si.workload(name)
+    say(f"[attn-every-row] {w.name} N={w.seq_len} H={w.num_heads}: GPU run")
+    Q, K, V = inputs(w)
+    o = run_attention(w, Q, K, V)
+    say(f"[attn-every-row] {w.name}: oracle over {w.num_heads} x {w.seq_len} rows")
+    t0 = time.time()
+    st = compare_all_rows(w, Q, K, V, masks_of(w), o)
+    say(f"  {name}: max_abs={st['max_abs']:.3e} mean_abs={st['mean_abs']:.3e} "
+        f"rel_l2={st['rel_l2']:.3e} over {st['elements']} elements; oracle "
+        f"{time.time() - t0:.1f} s on {len(__import__('os').sched_getaffinity(0))} cores")
+    assert st["finite"]
+    assert st["max_abs"] <= TOL_MAX and st["mean_abs"] <= TOL_MEAN, st
+    assert st["rel_l2"] <= TOL_REL_L2, st
+
+
+# The exact masks at every swept tile pair: sampled rows of the full main
+# workload (the tile search may pick any of them).
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("bq,bk", si.SWEEP_TILES)
+def test_exact_tile_pairs_sampled_rows(bq, bk):
+    w = si.workload("main").with_tiles(bq, bk)
+    say(f"[attn-exact-pairs] {w.name}")
+    Q, K, V = inputs(si.workload("main"))
+    o = run_attention(w, Q, K, V)
+    rows = _sample_rows(w, 64, seed=bq * 1000 + bk + 7)
+    ref = oracle_rows(w, Q, K, V, masks_of(w), rows)
+    check(o[:, rows], ref, w.name)
 
 
 @pytest.mark.timeout(900)

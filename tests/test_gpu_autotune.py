@@ -18,7 +18,7 @@ from test_oracle_pins import RAGGED
 
 pytestmark = pytest.mark.gpu
 
-CANDIDATES = [(32, 32), (64, 64), (128, 96), (256, 128), (512, 256)]
+CANDIDATES = [(32, 32), (64, 64), (128, 96), (256, 64), (256, 128), (512, 64), (512, 256)]
 
 
 def test_autotune_picks_the_fastest_and_keeps_parity():

@@ -139,3 +139,24 @@ def test_routing_rejects_bad_rows():
             svg.svg_route_heads(q, k, v, w.frames, w.grid_h, w.grid_w, w.frame_window, w.band,
                                 rows)
         assert e.value.status == svg.ERR_INVALID_ARG
+
+
+def test_windows_beyond_the_sequence_match_whole_sequence_windows():
+    # A band or window as wide as int32 allows keeps every pair of its kind,
+    # like one as wide as the sequence: the call clamps both before the
+    # kernels' interval arithmetic, which would otherwise overflow.
+    w = RAGGED
+    Q, K, V = si.draw_qkv(w)
+    rows = si.draw_query_subset(w, 64, seed=5)
+    q, k, v = (to_device(x) for x in (Q, K, V))
+    big = 2 ** 31 - 1
+    say(f"[route-wide] N={w.seq_len}: W_f = W_s = {big}")
+    k1, e1 = svg.svg_route_heads(q, k, v, w.frames, w.grid_h, w.grid_w, big, big, rows,
+                                 sink_first_frame=w.sink)
+    k2, e2 = svg.svg_route_heads(q, k, v, w.frames, w.grid_h, w.grid_w, w.frames - 1,
+                                 w.tokens_per_frame - 1, rows, sink_first_frame=w.sink)
+    np.testing.assert_array_equal(e1, e2)
+    assert k1 == k2
+    wide = si.Workload(w.name + "-wide", w.frames, w.grid_h, w.grid_w, w.head_kinds,
+                       w.head_dim, big, big, w.sink, w.tile_q, w.tile_k, False, w.seed)
+    _compare(wide, Q, K, V, rows, "int32-wide windows")

@@ -80,6 +80,9 @@ def _golden_workloads():
     out = [si.workload("main"), si.workload("dense"), si.workload("1440p")]
     ta = si.workload("tile-aligned")
     out += [ta.with_tiles(bq, bk) for bq, bk in si.SWEEP_TILES]
+    main = si.workload("main")
+    out += [main.with_tiles(bq, bk) for bq, bk in si.SWEEP_TILES
+            if (bq, bk) != (main.tile_q, main.tile_k)]
     return out
 
 

@@ -355,3 +355,40 @@ def test_kernel_layout_round_trip_and_coordinates():
     f, s = oracle.kernel_coords(p, "temporal", np.arange(2 * p.frames))
     assert f.tolist() == list(range(p.frames)) * 2
     assert s.tolist() == [0] * p.frames + [1] * p.frames
+
+
+# Executed tiles per head of the exact main masks at every swept tile pair,
+# (spatial, temporal), and the BOUNDARY tiles among them: the table computed
+# from the mask definitions alone. The golden digests the GPU maps are
+# compared with must carry the same figures.
+EXACT_SWEEP_EXECUTED = {
+    (128, 64): (294_320, 268_327), (128, 128): (147_597, 134_405),
+    (128, 256): (74_305, 67_730), (256, 64): (147_751, 134_755),
+    (256, 128): (74_094, 67_498), (256, 256): (37_301, 34_126),
+    (512, 64): (74_213, 67_830), (512, 128): (37_215, 33_975),
+    (512, 256): (18_734, 17_176),
+}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("bq,bk", si.SWEEP_TILES)
+def test_exact_main_sweep_executed_tiles(bq, bk):
+    import json
+    import os
+    F, S, Wf, Ws = 21, 3600, 4, 700
+    N = F * S
+    sp = interval_classes(interval_tile_counts(F, S, "spatial", Wf, Ws, True, bq, bk), N, bq, bk)
+    tp = interval_classes(interval_tile_counts(F, S, "temporal", Wf, Ws, True, bq, bk), N, bq, bk)
+    lo, hi, a, b = temporal_hull(F, S, Ws, bq, bk)
+    t_full = sum(int((tp[q, lo[q]:hi[q] + 1] == 1).sum()) for q in range(tp.shape[0]))
+    t_bnd = sum(int((tp[q, lo[q]:hi[q] + 1] == 2).sum()) for q in range(tp.shape[0]))
+    t_sink = int((-(-a // bk)).sum() + (-(-(S - b) // bk)).sum())
+    s_full, s_bnd = int((sp == 1).sum()), int((sp == 2).sum())
+    assert (s_full + s_bnd, t_full + t_bnd + t_sink) == EXACT_SWEEP_EXECUTED[(bq, bk)]
+    here = os.path.dirname(os.path.abspath(__file__))
+    with open(os.path.join(here, "golden", "tilemaps.json")) as f:
+        g = json.load(f)
+    key = "main@256x128" if (bq, bk) == (256, 128) else f"main-{bq}x{bk}@{bq}x{bk}"
+    gs, gt = g[key]["kinds"]["spatial"]["stats"], g[key]["kinds"]["temporal"]["stats"]
+    assert (gs["exec_full"], gs["exec_boundary"], gs["exec_sink"]) == (s_full, s_bnd, 0)
+    assert (gt["exec_full"], gt["exec_boundary"], gt["exec_sink"]) == (t_full, t_bnd, t_sink)
