@@ -283,6 +283,27 @@ svg_status svg_route_heads(const svg_mask_spec* spec, const void* q,
                            float scale, const int32_t* rows, int32_t n_rows,
                            void* stream, float* err, int32_t* kinds);
 
+/* svg_route_heads without any allocation, for callers that cannot allocate
+ * device memory during the call (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation). Same arguments, results and
+ * errors as svg_route_heads, plus UNSUPPORTED when the work does not fit
+ * the library's scratch. The scratch is one 48 MiB device array per GPU
+ * (kept until the process ends), used one head at a time: it must hold one
+ * head's V^T (head_dim x (N + 128) bf16 values at most), the sampled rows,
+ * their partial results over at least one key split (n_rows x 3 x
+ * (head_dim + 2) floats per split) and their row errors, plus 12 bytes per
+ * head; at head_dim 128 a head of up to about 130,000 tokens fits with a
+ * few thousand sampled rows. Every call on one GPU uses the same array: two
+ * calls that overlap in time on one GPU (other host threads, other streams)
+ * race and give wrong results; calls queued one after another are safe.
+ * Nothing in the array needs clearing between calls: every value a call
+ * reads, it has written. Synchronous, like svg_route_heads. */
+svg_status svg_route_heads_noalloc(const svg_mask_spec* spec, const void* q,
+                                   const void* k, const void* v,
+                                   int32_t head_dim, float scale,
+                                   const int32_t* rows, int32_t n_rows,
+                                   void* stream, float* err, int32_t* kinds);
+
 /* Token re-ordering between the original frame-major order t = f*S + s and
  * each head's kernel layout (temporal heads: p = s*F + f; other heads: p = t,
  * a plain copy). src, dst: device bf16 [num_heads][frames*tokens_per_frame]

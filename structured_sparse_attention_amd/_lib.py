@@ -36,8 +36,9 @@ _KIND_NAMES = {"spatial": HEAD_SPATIAL, "temporal": HEAD_TEMPORAL, "dense": HEAD
 EXPORTED = (
     "svg_build_tile_map", "svg_tile_map_rebuild", "svg_tile_map_info_get",
     "svg_tile_map_stats", "svg_tile_map_copy_classes", "svg_tile_map_copy_schedule",
-    "svg_tile_map_plan_info", "svg_tile_map_destroy", "svg_attn_fwd", "svg_autotune_tiles", "svg_route_heads",
-    "svg_permute_tokens", "svg_last_error", "svg_abi_version",
+    "svg_tile_map_plan_info", "svg_tile_map_destroy", "svg_attn_fwd", "svg_autotune_tiles",
+    "svg_route_heads", "svg_route_heads_noalloc", "svg_permute_tokens", "svg_last_error",
+    "svg_abi_version",
 )
 
 
@@ -107,6 +108,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      pI32]),
         "svg_route_heads": (I32, [ctypes.POINTER(MaskSpec), P, P, P, I32, ctypes.c_float, pI32,
                                   I32, P, ctypes.POINTER(ctypes.c_float), pI32]),
+        "svg_route_heads_noalloc": (I32, [ctypes.POINTER(MaskSpec), P, P, P, I32, ctypes.c_float,
+                                          pI32, I32, P, ctypes.POINTER(ctypes.c_float), pI32]),
         "svg_permute_tokens": (I32, [P, P, I32, I32, I32, I32, pI32, I32, P]),
         "svg_last_error": (ctypes.c_char_p, []),
         "svg_abi_version": (I32, []),
@@ -274,12 +277,13 @@ def svg_autotune_tiles(q, k, v, o, frames: int, grid_h: int, grid_w: int,
 
 def svg_route_heads(q, k, v, frames: int, grid_h: int, grid_w: int, frame_window: int,
                     temporal_band: int, rows, sink_first_frame: bool = True,
-                    scale: Optional[float] = None, stream=None):
+                    scale: Optional[float] = None, stream=None, no_alloc: bool = False):
     """Route each head to the spatial or temporal mask from sampled query rows.
 
     q, k, v: bf16 [H, N, d] in the original frame-major order; rows: original
     query indices. Returns (kinds: list of "spatial"/"temporal", err: float32
-    [H, 2] numpy array of the spatial and temporal mean squared errors)."""
+    [H, 2] numpy array of the spatial and temporal mean squared errors).
+    no_alloc: use svg_route_heads_noalloc (the library's static scratch)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _bf16_tensor(t, n)
     H, N, d = q.shape
@@ -295,10 +299,10 @@ def svg_route_heads(q, k, v, frames: int, grid_h: int, grid_w: int, frame_window
                     1 if sink_first_frame else 0, ROUND_EXACT)
     err = np.zeros((H, 2), dtype=np.float32)
     kinds = np.zeros(H, dtype=np.int32)
-    _check(load().svg_route_heads(ctypes.byref(spec), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                  d, float(scale), _i32p(r), len(r), _stream(stream),
-                                  err.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
-                                  _i32p(kinds)))
+    fn = load().svg_route_heads_noalloc if no_alloc else load().svg_route_heads
+    _check(fn(ctypes.byref(spec), q.data_ptr(), k.data_ptr(), v.data_ptr(), d, float(scale),
+              _i32p(r), len(r), _stream(stream),
+              err.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _i32p(kinds)))
     names = {HEAD_SPATIAL: "spatial", HEAD_TEMPORAL: "temporal"}
     return [names[int(x)] for x in kinds], err
 

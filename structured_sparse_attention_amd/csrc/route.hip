@@ -30,6 +30,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 namespace svg {
 namespace {
@@ -402,7 +403,8 @@ int route_slots(int32_t D) {
   return cus * per;
 }
 
-RouteLayout route_layout(int64_t N, int32_t H, int32_t D, int32_t n_rows, int32_t slots) {
+RouteLayout route_layout(int64_t N, int32_t H, int32_t D, int32_t n_rows, int32_t slots,
+                         int64_t max_split) {
   RouteLayout L;
   L.pitch = (N + 63) / 64 * 64 + 64;  // a multiple of 64; keys past N read zeros
   const int64_t pairs = ((n_rows + RQ - 1) / RQ + 1) / 2;  // workgroups per (head, split)
@@ -422,6 +424,7 @@ RouteLayout route_layout(int64_t N, int32_t H, int32_t D, int32_t n_rows, int32_
     }
   }
   ns = std::max<int64_t>(1, std::min<int64_t>(ns, kmax));
+  if (max_split > 0) ns = std::min(ns, max_split);
   L.split_len = ((N + ns - 1) / ns + RK - 1) / RK * RK;
   L.n_split = (N + L.split_len - 1) / L.split_len;
   const int64_t a = 256;
@@ -478,6 +481,72 @@ hipError_t launch_route(const void* q, const void* k, const void* v, char* scrat
   }
   hipLaunchKernelGGL(route_decide, dim3(H), dim3(256), 0, stream, p, (const double*)row_err, D);
   return hipGetLastError();
+}
+
+}  // namespace svg
+
+// ---- Routing without allocation (svg_route_heads_noalloc) ----------------
+// One scratch array per device, held until the process ends. Host code
+// never passes its name to a kernel (in host code it stands for a host-side
+// symbol); the device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+static __device__ __align__(256) char scratch[svg::kRouteStaticBytes];
+
+namespace svg {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxDevices] = {};
+}  // namespace
+
+hipError_t route_static_scratch(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_dev[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
+RouteLayout route_static_layout(int64_t N, int32_t H, int32_t D, int32_t n_rows, int32_t slots,
+                                int64_t* results_off) {
+  // One head at a time: V^T, rows, partial results and row errors of one
+  // head, then every head's (errors, kind); the key splits shrink until the
+  // layout fits the array.
+  const int64_t kmax = (N + 31) / 32;
+  RouteLayout L = route_layout(N, 1, D, n_rows, slots, 0);
+  for (int64_t ns = L.n_split; ns >= 1; --ns) {
+    L = route_layout(N, 1, D, n_rows, slots, std::min(ns, kmax));
+    if (L.bytes + (int64_t)H * 16 + 256 <= kRouteStaticBytes) break;
+  }
+  *results_off = (L.bytes + 255) / 256 * 256;
+  return L;
+}
+
+hipError_t launch_route_static(const void* q, const void* k, const void* v, char* sc,
+                               const RouteLayout& L, int64_t results_off, int64_t N, int32_t F,
+                               int32_t S, int32_t H, int32_t D, int32_t W_f, int32_t W_s,
+                               int32_t sink, float scale, int32_t n_rows, hipStream_t stream) {
+  const size_t head = (size_t)N * D * 2;
+  for (int32_t h = 0; h < H; ++h) {
+    // this head's (errors, kind) go to the shared result area
+    RouteLayout Lh = L;
+    Lh.err_off = results_off + (int64_t)h * 8;
+    Lh.kind_off = results_off + (int64_t)H * 8 + (int64_t)h * 4;
+    const hipError_t e =
+        launch_route((const char*)q + h * head, (const char*)k + h * head,
+                     (const char*)v + h * head, sc, Lh, N, F, S, 1, D, W_f, W_s, sink, scale,
+                     n_rows, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace svg

@@ -194,6 +194,54 @@ svg_status run_build(svg_tile_map* m, hipStream_t stream) {
   return ok();
 }
 
+// Arguments of a routing call after validation: N, S and the windows
+// clamped to the sequence.
+struct RouteArgs {
+  int64_t N = 0;
+  int32_t S = 0, W_f = 0, W_s = 0;
+};
+
+svg_status route_validate(const svg_mask_spec* spec, const void* q, const void* k, const void* v,
+                          int32_t head_dim, float scale, const int32_t* rows, int32_t n_rows,
+                          const int32_t* kinds, RouteArgs& out) {
+  if (!spec) return fail(SVG_ERR_INVALID_ARG, "spec is NULL");
+  if (!q || !k || !v) return fail(SVG_ERR_INVALID_ARG, "q, k and v must be non-NULL");
+  if (!rows || !kinds) return fail(SVG_ERR_INVALID_ARG, "rows and kinds must be non-NULL");
+  if (spec->frames < 1 || spec->grid_h < 1 || spec->grid_w < 1)
+    return fail(SVG_ERR_INVALID_ARG, "frames, grid_h and grid_w must be >= 1");
+  const int64_t S = (int64_t)spec->grid_h * spec->grid_w;
+  const int64_t N = S * spec->frames;
+  if (S > (1 << 30) || N > (1 << 30))
+    return fail(SVG_ERR_INVALID_ARG, "sequence of %lld tokens exceeds 2^30", (long long)N);
+  if (spec->num_heads < 1 || spec->num_heads > 4096)
+    return fail(SVG_ERR_INVALID_ARG, "num_heads %d outside [1, 4096]", spec->num_heads);
+  if (spec->frame_window < 0 || spec->temporal_band < 0)
+    return fail(SVG_ERR_INVALID_ARG, "frame_window and temporal_band must be >= 0");
+  if (n_rows < 1 || n_rows > 65536)
+    return fail(SVG_ERR_INVALID_ARG, "n_rows %d outside [1, 65536]", n_rows);
+  for (int32_t i = 0; i < n_rows; ++i)
+    if (rows[i] < 0 || rows[i] >= N)
+      return fail(SVG_ERR_INVALID_ARG, "rows[%d] = %d outside [0, %lld)", i, rows[i],
+                  (long long)N);
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(SVG_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SVG_ERR_UNSUPPORTED, "head_dim %d: supported are 64 and 128", head_dim);
+  if (N * head_dim * 2 >= ((int64_t)1 << 31))
+    return fail(SVG_ERR_UNSUPPORTED, "one head of %lld x %d bf16 values exceeds 2 GiB",
+                (long long)N, head_dim);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(SVG_ERR_ALIGNMENT, "q, k and v must be 16-byte aligned");
+  out.N = N;
+  out.S = (int32_t)S;
+  // Windows wider than the sequence behave like the sequence (as in
+  // svg_build_tile_map); clamping keeps the kernels' interval arithmetic in
+  // 32-bit range.
+  out.W_f = spec->frame_window < spec->frames ? spec->frame_window : spec->frames;
+  out.W_s = spec->temporal_band < S ? spec->temporal_band : (int32_t)S;
+  return SVG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -615,41 +663,12 @@ svg_status svg_autotune_tiles(const svg_mask_spec* spec, const void* q, const vo
 svg_status svg_route_heads(const svg_mask_spec* spec, const void* q, const void* k, const void* v,
                            int32_t head_dim, float scale, const int32_t* rows, int32_t n_rows,
                            void* stream, float* err, int32_t* kinds) {
-  if (!spec) return fail(SVG_ERR_INVALID_ARG, "spec is NULL");
-  if (!q || !k || !v) return fail(SVG_ERR_INVALID_ARG, "q, k and v must be non-NULL");
-  if (!rows || !kinds) return fail(SVG_ERR_INVALID_ARG, "rows and kinds must be non-NULL");
-  if (spec->frames < 1 || spec->grid_h < 1 || spec->grid_w < 1)
-    return fail(SVG_ERR_INVALID_ARG, "frames, grid_h and grid_w must be >= 1");
-  const int64_t S = (int64_t)spec->grid_h * spec->grid_w;
-  const int64_t N = S * spec->frames;
-  if (S > (1 << 30) || N > (1 << 30))
-    return fail(SVG_ERR_INVALID_ARG, "sequence of %lld tokens exceeds 2^30", (long long)N);
-  if (spec->num_heads < 1 || spec->num_heads > 4096)
-    return fail(SVG_ERR_INVALID_ARG, "num_heads %d outside [1, 4096]", spec->num_heads);
-  if (spec->frame_window < 0 || spec->temporal_band < 0)
-    return fail(SVG_ERR_INVALID_ARG, "frame_window and temporal_band must be >= 0");
-  if (n_rows < 1 || n_rows > 65536)
-    return fail(SVG_ERR_INVALID_ARG, "n_rows %d outside [1, 65536]", n_rows);
-  for (int32_t i = 0; i < n_rows; ++i)
-    if (rows[i] < 0 || rows[i] >= N)
-      return fail(SVG_ERR_INVALID_ARG, "rows[%d] = %d outside [0, %lld)", i, rows[i],
-                  (long long)N);
-  if (!(scale > 0.f) || !std::isfinite(scale))
-    return fail(SVG_ERR_INVALID_ARG, "scale must be positive and finite");
-  if (head_dim != 64 && head_dim != 128)
-    return fail(SVG_ERR_UNSUPPORTED, "head_dim %d: supported are 64 and 128", head_dim);
-  if (N * head_dim * 2 >= ((int64_t)1 << 31))
-    return fail(SVG_ERR_UNSUPPORTED, "one head of %lld x %d bf16 values exceeds 2 GiB",
-                (long long)N, head_dim);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
-    return fail(SVG_ERR_ALIGNMENT, "q, k and v must be 16-byte aligned");
+  RouteArgs ra;
+  const svg_status vs = route_validate(spec, q, k, v, head_dim, scale, rows, n_rows, kinds, ra);
+  if (vs != SVG_OK) return vs;
   const int32_t H = spec->num_heads;
-  // Windows wider than the sequence behave like the sequence (as in
-  // svg_build_tile_map); clamping keeps the kernels' interval arithmetic in
-  // 32-bit range.
-  const int32_t W_f = spec->frame_window < spec->frames ? spec->frame_window : spec->frames;
-  const int32_t W_s = spec->temporal_band < S ? spec->temporal_band : (int32_t)S;
-  const svg::RouteLayout L = svg::route_layout(N, H, head_dim, n_rows, svg::route_slots(head_dim));
+  const svg::RouteLayout L =
+      svg::route_layout(ra.N, H, head_dim, n_rows, svg::route_slots(head_dim));
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* scratch = nullptr;
   hipError_t e = hipMalloc(reinterpret_cast<void**>(&scratch), (size_t)L.bytes);
@@ -658,9 +677,8 @@ svg_status svg_route_heads(const svg_mask_spec* spec, const void* q, const void*
   std::vector<float> err_h((size_t)H * 2);
   e = hipMemcpyAsync(scratch + L.rows_off, rows, (size_t)n_rows * 4, hipMemcpyHostToDevice, st);
   if (e == hipSuccess)
-    e = svg::launch_route(q, k, v, scratch, L, N, spec->frames, (int32_t)S, H, head_dim,
-                          W_f, W_s, spec->sink_first_frame ? 1 : 0,
-                          scale, n_rows, st);
+    e = svg::launch_route(q, k, v, scratch, L, ra.N, spec->frames, ra.S, H, head_dim, ra.W_f,
+                          ra.W_s, spec->sink_first_frame ? 1 : 0, scale, n_rows, st);
   if (e == hipSuccess)
     e = hipMemcpyAsync(err_h.data(), scratch + L.err_off, err_h.size() * 4,
                        hipMemcpyDeviceToHost, st);
@@ -671,6 +689,43 @@ svg_status svg_route_heads(const svg_mask_spec* spec, const void* q, const void*
   if (e != hipSuccess) return hip_fail(e, "routing kernels");
   if (fe != hipSuccess) return hip_fail(fe, "hipFree");
   if (err) std::memcpy(err, err_h.data(), err_h.size() * 4);
+  return ok();
+}
+
+svg_status svg_route_heads_noalloc(const svg_mask_spec* spec, const void* q, const void* k,
+                                   const void* v, int32_t head_dim, float scale,
+                                   const int32_t* rows, int32_t n_rows, void* stream, float* err,
+                                   int32_t* kinds) {
+  RouteArgs ra;
+  const svg_status vs = route_validate(spec, q, k, v, head_dim, scale, rows, n_rows, kinds, ra);
+  if (vs != SVG_OK) return vs;
+  const int32_t H = spec->num_heads;
+  int64_t res_off = 0;
+  const svg::RouteLayout L =
+      svg::route_static_layout(ra.N, H, head_dim, n_rows, svg::route_slots(head_dim), &res_off);
+  const int64_t need = res_off + (int64_t)H * 12;
+  if (need > svg::kRouteStaticBytes)
+    return fail(SVG_ERR_UNSUPPORTED,
+                "routing without allocation needs %lld bytes of scratch for one head of %lld "
+                "tokens, %d sampled rows and %d heads; the library's array holds %lld",
+                (long long)need, (long long)ra.N, n_rows, H, (long long)svg::kRouteStaticBytes);
+  char* sc = nullptr;
+  hipError_t e = svg::route_static_scratch(&sc);
+  if (e != hipSuccess) return hip_fail(e, "address of the routing scratch");
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  e = hipMemcpyAsync(sc + L.rows_off, rows, (size_t)n_rows * 4, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess)
+    e = svg::launch_route_static(q, k, v, sc, L, res_off, ra.N, spec->frames, ra.S, H, head_dim,
+                                 ra.W_f, ra.W_s, spec->sink_first_frame ? 1 : 0, scale, n_rows,
+                                 st);
+  // results to the caller's arrays: errors only when asked for
+  if (e == hipSuccess && err)
+    e = hipMemcpyAsync(err, sc + res_off, (size_t)H * 8, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(kinds, sc + res_off + (int64_t)H * 8, (size_t)H * 4,
+                       hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "routing kernels");
   return ok();
 }
 

@@ -117,8 +117,9 @@ struct RouteLayout {
   int64_t vt_off, rows_off, part_off, row_err_off, err_off, kind_off, bytes;
 };
 // slots: workgroups of the routing kernel the device holds at once (0 if
-// unknown), which sets the number of key splits.
-RouteLayout route_layout(int64_t N, int32_t H, int32_t D, int32_t n_rows, int32_t slots);
+// unknown), which sets the number of key splits; max_split > 0 caps them.
+RouteLayout route_layout(int64_t N, int32_t H, int32_t D, int32_t n_rows, int32_t slots,
+                         int64_t max_split = 0);
 // CUs x resident routing workgroups per CU on the current device, 0 on failure.
 int route_slots(int32_t D);
 // Queue the routing kernels; the sampled rows must already be at
@@ -127,6 +128,23 @@ hipError_t launch_route(const void* q, const void* k, const void* v, char* scrat
                         const RouteLayout& L, int64_t N, int32_t F, int32_t S, int32_t H,
                         int32_t D, int32_t W_f, int32_t W_s, int32_t sink, float scale,
                         int32_t n_rows, hipStream_t stream);
+
+// Routing without allocation: a per-device static scratch of
+// kRouteStaticBytes, used one head at a time.
+constexpr int64_t kRouteStaticBytes = 48ll << 20;
+// The calling thread's current device's scratch (device address).
+hipError_t route_static_scratch(char** out);
+// Layout of one head's routing in the scratch, and the offset of the
+// results of all heads (float [H][2] errors, then int32 [H] kinds) after it.
+// The caller checks results_off + H * 12 <= kRouteStaticBytes.
+RouteLayout route_static_layout(int64_t N, int32_t H, int32_t D, int32_t n_rows, int32_t slots,
+                                int64_t* results_off);
+// Queue the routing kernels head by head in the scratch `sc`; the sampled
+// rows must already be at sc + L.rows_off.
+hipError_t launch_route_static(const void* q, const void* k, const void* v, char* sc,
+                               const RouteLayout& L, int64_t results_off, int64_t N, int32_t F,
+                               int32_t S, int32_t H, int32_t D, int32_t W_f, int32_t W_s,
+                               int32_t sink, float scale, int32_t n_rows, hipStream_t stream);
 
 // kinds: host array [H]; one launch per head.
 hipError_t launch_permute_tokens(const void* src, void* dst, int32_t F,

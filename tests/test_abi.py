@@ -138,14 +138,15 @@ def test_autotune_rejects_bad_arguments_before_hip(lib):
     assert f(*args(d=96)) == svg.ERR_UNSUPPORTED       # head_dim 96 has no kernel
 
 
-def test_route_rejects_bad_arguments_before_hip(lib):
+@pytest.mark.parametrize("name", ["svg_route_heads", "svg_route_heads_noalloc"])
+def test_route_rejects_bad_arguments_before_hip(lib, name):
     spec = _lib.MaskSpec(4, 8, 8, 2, None, 1, 8, 1, 0)
     p = 1 << 20  # never dereferenced: validation fails first
     rows = np.array([0, 5, 255], dtype=np.int32)
     bad = np.array([0, 256], dtype=np.int32)
     ip = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     kinds = np.zeros(2, dtype=np.int32)
-    f = lib.svg_route_heads
+    f = getattr(lib, name)
     assert f(None, p, p, p, 64, 0.125, ip(rows), 3, None, None, ip(kinds)) == svg.ERR_INVALID_ARG
     assert f(ctypes.byref(spec), None, p, p, 64, 0.125, ip(rows), 3, None, None,
              ip(kinds)) == svg.ERR_INVALID_ARG
