@@ -40,7 +40,10 @@ sys.path.insert(0, ROOT)
 
 # MI355X dense bf16 MFMA peak: 256 CU x 2.4 GHz x 4096 FLOP/clk (the published 2.5 PFLOP/s)
 PEAK_BF16_TFLOPS = 2516.6
-KERNEL_SRC = os.path.join(ROOT, "structured_sparse_attention_amd", "csrc", "attn_fwd.hip")
+# the sources that decide the attention kernel's memory traffic: the kernel
+# and the launch plan
+TRAFFIC_SRC = [os.path.join(ROOT, "structured_sparse_attention_amd", "csrc", f)
+               for f in ("attn_fwd.hip", "plan.cpp", "plan.hpp", "svg_internal.hpp", "svg_api.cpp")]
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_fwd_main_hbm_traffic.md")
 METRIC = "sparse attn fwd ms + effective TFLOP/s (retained pairs) at 75,600 tok×10 heads×d128"
 
@@ -245,9 +248,23 @@ def gemm_reference(n=16384, reps=5):
             "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
 
 
+def heads_desc(w):
+    """The workload's head kinds and mask parameters, for the config string."""
+    n = {k: w.head_kinds.count(k) for k in ("spatial", "temporal", "dense")}
+    parts = []
+    if n["spatial"]:
+        parts.append(f"{n['spatial']} spatial W_f={w.frame_window}")
+    if n["temporal"]:
+        parts.append(f"{n['temporal']} temporal W_s={w.band}")
+    if n["dense"]:
+        parts.append(f"{n['dense']} dense")
+    return ", ".join(parts) + (", frame-0 sink" if w.sink and (n["spatial"] or n["temporal"])
+                               else "")
+
+
 def measured_traffic():
     """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source; else None."""
+    on the current kernel and plan sources; else None."""
     if not os.path.exists(TRAFFIC_PROFILE):
         return None
     text = open(TRAFFIC_PROFILE).read()
@@ -255,8 +272,10 @@ def measured_traffic():
     b = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
     if not m or not b:
         return None
-    cur = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    return int(b.group(1)) if m.group(1) == cur else None
+    h = hashlib.sha256()
+    for f in TRAFFIC_SRC:
+        h.update(open(f, "rb").read())
+    return int(b.group(1)) if m.group(1) == h.hexdigest() else None
 
 
 def main():
@@ -391,8 +410,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: F={w.frames} {w.grid_h}x{w.grid_w} "
-                               f"N={w.seq_len} H={w.num_heads} (5 spatial W_f={w.frame_window}, "
-                               f"5 temporal W_s={w.band}, frame-0 sink) d={w.head_dim} "
+                               f"N={w.seq_len} H={w.num_heads} ({heads_desc(w)}) d={w.head_dim} "
                                f"tiles {w.tile_q}x{w.tile_k} "
                                f"{'tile-aligned' if w.tile_aligned else 'exact'}",
                    "global_batch": 1, "seq_len": w.seq_len, "parallelism": "single-gpu"},
