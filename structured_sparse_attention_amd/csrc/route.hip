@@ -10,19 +10,28 @@
 // spatial one on a tie). Inputs are in the original frame-major order.
 //
 // Four kernels:
-//   vt_kernel       V -> V^T per head ([d][pitch], zero padded), so that a
-//                   lane fetches 8 consecutive keys of one dim with one
-//                   16-byte load. HBM-bound, one read and one write of V.
-//   route_partial   one wave per (head, mask, 32 sampled rows, key split):
-//                   per step of 32 keys S^T = K Q^T with
-//                   v_mfma_f32_32x32x16_bf16 (K from LDS, Q in VGPRs), the
-//                   mask's keep bits, an online softmax (fp32, P rounded to
-//                   bf16) and O^T += V^T P^T (V^T from LDS). One mask per
-//                   wave keeps one O^T in registers (three would spill); the
-//                   six waves of a workgroup share the K and V^T of a step.
-//                   Writes (max, sum, O^T) per (row, split, mask).
+//   vt_kernel       V -> V^T per head ([d][pitch], zero padded), keys
+//                   reordered inside each 32-key chunk to the order in which
+//                   the MFMA below holds its weights, so that a lane fetches
+//                   its 8 keys of one dim with one 16-byte load. HBM-bound,
+//                   one read and one write of V.
+//   route_partial   one wave per (head, 16 sampled rows, key split), eight
+//                   waves to a workgroup sharing each step's K rows and V^T
+//                   slice through LDS. Per step of 64 keys: S^T = K Q^T once
+//                   (v_mfma_f32_16x16x32_bf16, K from LDS, Q in VGPRs), the
+//                   dense online-softmax weights P (fp32, rounded to bf16),
+//                   the spatial and temporal weights as P with the masked
+//                   keys zeroed, and O^T += V^T P^T for all three (one V^T
+//                   fragment from LDS feeds three MFMAs). The three outputs
+//                   share the dense running maximum, so a mask's weights are
+//                   the dense ones; a mask whose kept weights would all fall
+//                   below fp32's range under that maximum is caught after the
+//                   merge and recomputed exactly. Writes (max, sum, O^T) per
+//                   (row, split, output).
 //   route_rows      one workgroup per (sampled row, head): merges the splits,
-//                   forms the three outputs and the row's squared errors.
+//                   forms the three outputs (the exact path where a mask's
+//                   merged sum is too small to trust) and the row's squared
+//                   errors.
 //   route_decide    one workgroup per head: sums the rows' errors (float64,
 //                   fixed order) and takes the decision.
 #include "svg_internal.hpp"
@@ -38,49 +47,58 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int RK = 32;  // keys per step
-constexpr int RQ = 32;  // sampled rows per wave
-constexpr int RW = 6;   // waves per workgroup: 3 masks x 2 row blocks, one key split
-
-struct RouteParams {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* vt;    // [H][D][pitch]
-  const int32_t* rows;   // [n_rows], original-order query indices
-  float* part;           // [H][n_rows][n_split][3][D + 2]
-  float* err;            // [H][2]
-  int32_t* kind;         // [H]
-  int32_t n_rows, N, F, S, W_f, W_s, sink, pitch, n_split, split_len;
-  float c;               // scale * log2(e)
-};
-
-// As in the attention kernel: with A row m of a 32-key block holding key
-// sigma(m), accumulator v of a lane is key 16*(v/8) + 8*(lane/32) + v%8, so
-// a lane's accumulators 8kk..8kk+7 are the B operand of the PV product for
-// keys 16kk..16kk+15.
-__device__ __forceinline__ int sigma(int m) {
-  return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
-}
+constexpr int RK = 64;  // keys per step
+constexpr int RQ = 16;  // sampled rows per wave
+constexpr int RW = 8;   // waves per workgroup (one block of RQ rows each), one key split
+// Running maxima may lag the true one by up to 2^kLazy before the
+// accumulators are rescaled (weights stay below 2^kLazy).
+constexpr float kLazy = 8.f;
+// A mask's merged weight sum, in units of the dense maximum, below which
+// its output is recomputed exactly: each lost weight is below 2^-126 and a
+// row has fewer than 2^31 keys, so above this bound the lost share is below
+// 2^-31.
+constexpr float kExactBelow = 0x1p-64f;
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const f32x2 x = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
-// The values of lanes (lane & 31) and (lane & 31) + 32: the two halves of a
-// row's keys.
-__device__ __forceinline__ void halves(float x, float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
+
+// Reductions over the four lanes of a row (lanes n, n + 16, n + 32, n + 48):
+// the 16-lane swap pairs rows {0,1} and {2,3} of the wave, the 32-lane swap
+// the two halves.
+__device__ __forceinline__ float row_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  a = __uint_as_float(r[0]);
-  b = __uint_as_float(r[1]);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// V^T of one head: thread (8-key group, 8-dim group) -> 8 loads, register
-// transpose, 8 stores; columns past N are zero.
+// Position 32c + 8gg + j of a V^T row holds key 32c + 4gg + j (j < 4) or
+// 32c + 16 + 4gg + j - 4 (j >= 4): the keys whose weights lane group gg of
+// the 16x16 MFMA holds for chunk c (accumulators of two 16-key blocks).
+__device__ __forceinline__ int64_t vt_key(int64_t pos) {
+  const int64_t j = pos & 7, gg = (pos >> 3) & 3;
+  return (pos & ~(int64_t)31) + 4 * gg + (j < 4 ? j : 12 + j);
+}
+
+// V^T of one head: thread (8-position group, 8-dim group) -> 8 loads,
+// register transpose, 8 stores; keys past N are zero.
 template <int D>
 __global__ __launch_bounds__(256) void vt_kernel(const uint4* __restrict__ v,
                                                  uint4* __restrict__ vt, int64_t total, int32_t N,
@@ -99,8 +117,9 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint4* __restrict__ v,
   u16x8 in[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
+    const int64_t key = vt_key(col0 + i);
     uint4 x = make_uint4(0, 0, 0, 0);
-    if (col0 + i < N) x = vh[(col0 + i) * DC + c];
+    if (key < N) x = vh[key * DC + c];
     in[i] = __builtin_bit_cast(u16x8, x);
   }
   uint4* dst = vt + ((h * D + 8 * c) * pitch + col0) / 8;
@@ -121,208 +140,369 @@ __device__ __forceinline__ uint32_t bit_range(int a, int b) {
   return hi & ~((1u << a) - 1u);
 }
 
-// Keep bits of the 32 keys key0 + j (frame fk0 and raster index sk0 at
-// j = 0) for a query at (fq, sq): x = 1 spatial, |fq - f| <= W_f; x = 2
-// temporal, |sq - s| <= W_s; either or frame 0 with the sink. With S >= 32
-// the keys span at most two frames, split at j = S - sk0, and each mask is
-// one frame test or one interval of j per frame; shorter frames take the
-// key-by-key path.
-__device__ __forceinline__ uint32_t mask_bits(const RouteParams& p, int x, int fq, int sq,
-                                              int fk0, int sk0) {
-  if (p.S >= 32) {
-    const int jw = p.S - sk0;  // first key of frame fk0 + 1
-    const uint32_t lo = jw >= 32 ? ~0u : ((1u << jw) - 1u);
-    auto frame_kept = [&](int f) { return abs(fq - f) <= p.W_f || (p.sink && f == 0); };
-    if (x == 1) return (frame_kept(fk0) ? lo : 0u) | (frame_kept(fk0 + 1) ? ~lo : 0u);
-    uint32_t m = (bit_range(sq - p.W_s - sk0, sq + p.W_s - sk0) & lo) |
-                 (bit_range(sq - p.W_s - sk0 + p.S, sq + p.W_s - sk0 + p.S) & ~lo);
-    if (p.sink && fk0 == 0) m |= lo;
+// A lane's 16 keep bits for the step's keys at relative positions [a, b]:
+// bit 4mb + i stands for key 16mb + g4 + i (g4 = 4 * (lane / 16)), the key
+// of the lane's accumulator i of 16-key block mb.
+__device__ __forceinline__ uint32_t lane_bits(int a, int b, int g4) {
+  a = max(a, -64);
+  b = min(b, 128);
+  const uint32_t w0 = bit_range(a, b) >> g4, w1 = bit_range(a - 32, b - 32) >> g4;
+  return (w0 & 0xFu) | ((w0 >> 12) & 0xF0u) | ((w1 & 0xFu) << 8) | ((w1 >> 4) & 0xF000u);
+}
+
+struct RouteParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;     // [H][N][D], read by the exact path
+  const uint16_t* vt;    // [H][D][pitch], keys reordered as vt_key states
+  const int32_t* rows;   // [n_rows], original-order query indices
+  float* part;           // [H][n_rows][n_split][3][D + 2]
+  float* err;            // [H][2]
+  int32_t* kind;         // [H]
+  int32_t n_rows, N, F, S, W_f, W_s, sink, pitch, n_split, split_len;
+  float c;               // scale * log2(e)
+};
+
+// Keep bits of the lane's 16 keys of the step at key0 (frame fk0, raster
+// index sk0) for the query at (fq, sq): x = 1 spatial, |fq - f| <= W_f;
+// x = 2 temporal, |sq - s| <= W_s; either or frame 0 with the sink. With
+// S >= 64 the keys span at most two frames, split at relative key jb, and
+// each mask keeps a whole frame or one interval of it; shorter frames take
+// the key-by-key path.
+__device__ __forceinline__ uint32_t lane_keep(const RouteParams& p, int x, int fq, int sq,
+                                              int key0, int fk0, int sk0, int g4) {
+  if (p.S >= RK) {
+    const int jb = p.S - sk0;  // first key of frame fk0 + 1
+    if (x == 1) {
+      auto kept = [&](int f) { return abs(fq - f) <= p.W_f || (p.sink && f == 0); };
+      const bool ka = kept(fk0);
+      if (jb >= RK) return ka ? 0xFFFFu : 0u;
+      const uint32_t lo = lane_bits(0, jb - 1, g4);
+      return (ka ? lo : 0u) | (kept(fk0 + 1) ? (~lo & 0xFFFFu) : 0u);
+    }
+    uint32_t m = (p.sink && fk0 == 0)
+                     ? lane_bits(0, jb - 1, g4)
+                     : lane_bits(max(sq - p.W_s - sk0, 0), min(sq + p.W_s - sk0, jb - 1), g4);
+    if (jb < RK) m |= lane_bits(max(sq - p.W_s + jb, jb), sq + p.W_s + jb, g4);
     return m;
   }
   uint32_t m = 0;
-  int f = fk0, sk = sk0;
-  for (int j = 0; j < 32; ++j) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int key = key0 + 16 * (v >> 2) + g4 + (v & 3);
+    const int f = key / p.S, s = key - f * p.S;
     const bool snk = p.sink && f == 0;
-    const bool kv = x == 1 ? (abs(fq - f) <= p.W_f || snk) : (abs(sq - sk) <= p.W_s || snk);
-    m |= (uint32_t)kv << j;
-    if (++sk == p.S) {
-      sk = 0;
-      ++f;
-    }
+    const bool kv = x == 1 ? (abs(fq - f) <= p.W_f || snk) : (abs(sq - s) <= p.W_s || snk);
+    m |= (uint32_t)kv << v;
   }
   return m;
 }
 
-// Workgroup: RW waves = 3 masks x 2 blocks of 32 sampled rows, all on the
-// same key split, sharing each step's K rows and V^T slice through LDS (the
-// global traffic is that of one wave, not six). A step's 32 K rows and
-// d x 32 V^T values are fetched into registers one step ahead and written to
-// LDS between two barriers. LDS rows are padded (K: 16 bytes per row; V^T:
-// 80-byte rows) so that 16 lanes reading 16 rows at one column hit 16
-// distinct 4-bank groups.
+// Workgroup: RW waves, each its own 16 sampled rows, all on one key split.
+// Stage (two buffers): the step's 64 K rows (2D + 32 bytes each) and the d
+// V^T rows of its 64 keys (160 bytes each). A wave's operand read takes 16
+// rows at 4 consecutive 16-byte columns; with these 32-byte pads the LDS
+// serves it without bank conflicts, where 16-byte pads (right for 32 rows
+// at 2 columns) cost a second pass (measured with the LDS bank-conflict
+// counter). Each thread fetches its share of the next step's stage into
+// registers one step ahead and writes it after the current step's compute;
+// one barrier per step.
 template <int D>
 __global__ __launch_bounds__(RW * 64) void route_partial(RouteParams p) {
-  constexpr int NDB = D / 32;
-  constexpr int KC = D / 8;               // 16-byte chunks per K row
-  constexpr int KROWB = 16 * (KC + 1);    // bytes per K row in LDS
-  constexpr int VROWB = 80;               // bytes per V^T row (32 keys + pad)
-  constexpr int NKCH = RK * KC, NCH = NKCH + D * (RK / 8);
-  constexpr int PER = (NCH + RW * 64 - 1) / (RW * 64);
+  constexpr int NKC = D / 32, NDB = D / 16;
+  constexpr int KROWB = 2 * D + 32, VROWB = 2 * RK + 32;
+  constexpr int KBYTES = RK * KROWB, STB = KBYTES + D * VROWB;
+  constexpr int KCH = D / 8;  // 16-byte chunks per K row
+  constexpr int NKCH = RK * KCH, NCH = NKCH + D * (RK / 8);
+  constexpr int NT = RW * 64, PER = NCH / NT;
+  static_assert(NKCH % NT == 0 && NCH % NT == 0 && PER <= 4, "whole staging rounds");
   constexpr float NEG_INF = -__builtin_huge_valf();
-  __shared__ __attribute__((aligned(16))) char lds[RK * KROWB + D * VROWB];
+  __shared__ __attribute__((aligned(16))) char lds[2 * STB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hl = lane >> 5, l32 = lane & 31;
-  const int x = wave % 3;                       // 0 dense, 1 spatial, 2 temporal
-  const int rb = blockIdx.y * 2 + wave / 3;     // block of 32 sampled rows
+  const int g = lane >> 4, n = lane & 15, g4 = 4 * g;
   const int split = blockIdx.x, h = blockIdx.z;
-
-  const size_t hoff = (size_t)h * p.N * D;
-  const int ri = rb * RQ + l32;
+  const int rb = blockIdx.y * RW + wave;  // block of 16 sampled rows
+  const bool wvalid = rb * RQ < p.n_rows;
+  const int ri = rb * RQ + n;
   const bool rvalid = ri < p.n_rows;
   const int t = rvalid ? p.rows[ri] : 0;
   const int fq = t / p.S, sq = t - fq * p.S;
-  bf16x8 qf[D / 16];
+  const size_t hoff = (size_t)h * p.N * D;
+  // B operand of S^T: row n, dims 32kc + 8g .. +7
+  bf16x8 qf[NKC];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
+  for (int kc = 0; kc < NKC; ++kc) {
     uint4 q4 = make_uint4(0, 0, 0, 0);
-    if (rvalid) q4 = *(const uint4*)(p.q + hoff + (size_t)t * D + 16 * ks + 8 * hl);
-    qf[ks] = __builtin_bit_cast(bf16x8, q4);
+    if (rvalid) q4 = *(const uint4*)(p.q + hoff + (size_t)t * D + 32 * kc + 8 * g);
+    qf[kc] = __builtin_bit_cast(bf16x8, q4);
   }
   const uint16_t* kh = p.k + hoff;
   const uint16_t* vth = p.vt + (size_t)h * D * p.pitch;
 
-  // chunk c of a step: K row m (key sigma(m)), chunk c % KC; or V^T dim
-  // (c - NKCH) / 4, keys 8 * ((c - NKCH) % 4) .. +7
-  static_assert(PER <= 3, "at most three staged chunks per thread");
-  uint4 pre0 = make_uint4(0, 0, 0, 0), pre1 = pre0, pre2 = pre0;
+  // chunk c of a stage: K row c / KCH (key0 + row, clamped to N - 1; masked),
+  // 16 bytes c % KCH; then V^T dim (c - NKCH) / 8, positions 8 * (c % 8) .. +7
+  static_assert(PER == 2 || PER == 4, "two or four staged chunks per thread");
+  uint4 pre0, pre1, pre2, pre3;  // separate values: an array here would live in scratch
   auto fetch1 = [&](int key0, int j, uint4& r) __attribute__((always_inline)) {
-    const int c = tid + j * RW * 64;
-    if (c < NKCH) {
-      const int m = c / KC, ch = c - m * KC;
-      const int key = min(key0 + sigma(m), p.N - 1);
-      r = *(const uint4*)(kh + (size_t)key * D + 8 * ch);
-    } else if (c < NCH) {
-      const int cv = c - NKCH, dim = cv >> 2, g = cv & 3;
-      r = *(const uint4*)(vth + (size_t)dim * p.pitch + key0 + 8 * g);
+    const int c = tid + j * NT;
+    if (j < NKCH / NT) {
+      const int key = min(key0 + c / KCH, p.N - 1);
+      r = *(const uint4*)(kh + (size_t)key * D + 8 * (c % KCH));
+    } else {
+      const int cv = c - NKCH;
+      r = *(const uint4*)(vth + (size_t)(cv >> 3) * p.pitch + key0 + 8 * (cv & 7));
     }
   };
-  auto store1 = [&](int j, const uint4& r) __attribute__((always_inline)) {
-    const int c = tid + j * RW * 64;
-    if (c < NKCH) {
-      const int m = c / KC, ch = c - m * KC;
-      *(uint4*)(lds + m * KROWB + 16 * ch) = r;
-    } else if (c < NCH) {
-      const int cv = c - NKCH, dim = cv >> 2, g = cv & 3;
-      *(uint4*)(lds + RK * KROWB + dim * VROWB + 16 * g) = r;
+  auto store1 = [&](char* buf, int j, const uint4& r) __attribute__((always_inline)) {
+    const int c = tid + j * NT;
+    if (j < NKCH / NT) {
+      *(uint4*)(buf + (c / KCH) * KROWB + 16 * (c % KCH)) = r;
+    } else {
+      const int cv = c - NKCH;
+      *(uint4*)(buf + KBYTES + (cv >> 3) * VROWB + 16 * (cv & 7)) = r;
     }
   };
   auto fetch = [&](int key0) __attribute__((always_inline)) {
     fetch1(key0, 0, pre0);
-    if constexpr (PER > 1) fetch1(key0, 1, pre1);
-    if constexpr (PER > 2) fetch1(key0, 2, pre2);
+    fetch1(key0, 1, pre1);
+    if constexpr (PER == 4) {
+      fetch1(key0, 2, pre2);
+      fetch1(key0, 3, pre3);
+    }
   };
-  auto store = [&]() __attribute__((always_inline)) {
-    store1(0, pre0);
-    if constexpr (PER > 1) store1(1, pre1);
-    if constexpr (PER > 2) store1(2, pre2);
+  auto store = [&](char* buf) __attribute__((always_inline)) {
+    store1(buf, 0, pre0);
+    store1(buf, 1, pre1);
+    if constexpr (PER == 4) {
+      store1(buf, 2, pre2);
+      store1(buf, 3, pre3);
+    }
   };
 
-  float m = NEG_INF, l = 0.f;
-  f32x16 o[NDB];
+  float m = NEG_INF, ld = 0.f, ls = 0.f, lt = 0.f;  // lane partial sums
+  f32x4 od[NDB], os[NDB], ot[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
+    for (int i = 0; i < 4; ++i) od[db][i] = os[db][i] = ot[db][i] = 0.f;
 
   const int k0 = split * p.split_len, k1 = min(p.N, k0 + p.split_len);
   int fk0 = k0 / p.S, sk0 = k0 - fk0 * p.S;  // (frame, raster index) of key0
   fetch(k0);
-  for (int key0 = k0; key0 < k1; key0 += RK, sk0 += RK) {
+  store(lds);
+  if (k0 + RK < k1) fetch(k0 + RK);
+  __syncthreads();
+  int it = 0;
+  for (int key0 = k0; key0 < k1; key0 += RK, ++it) {
+    const char* buf = lds + (it & 1) * STB;
+    if (wvalid) {
+      // S^T = K Q^T: accumulator i of block mb is key 16mb + 4g + i of row n
+      // every K fragment is read before the first MFMA, so that the reads'
+      // latencies overlap
+      bf16x8 ka[4][NKC];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+          ka[mb][kc] = *(const bf16x8*)(buf + (16 * mb + n) * KROWB + 64 * kc + 16 * g);
+      f32x4 s[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[mb][i] = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[mb][kc], qf[kc], s[mb], 0, 0, 0);
+      // V^T fragments of the first 32 keys, read while the weights are formed
+      bf16x8 va[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        va[db] = *(const bf16x8*)(buf + KBYTES + (16 * db + n) * VROWB + 16 * g);
+      const int nval = k1 - key0;  // keys of the split left (the step's are valid below it)
+      float mx = NEG_INF;
+      if (nval >= RK) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v >> 2][v & 3]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (16 * (v >> 2) + g4 + (v & 3) < nval) mx = fmaxf(mx, s[v >> 2][v & 3]);
+      }
+      mx = row_max4(mx) * p.c;
+      // lazy rescale: rows whose maximum rose by more than 2^kLazy take it
+      const bool grow = mx > m + kLazy;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float mn = grow ? mx : m;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
+        m = mn;
+        ld *= alpha;
+        ls *= alpha;
+        lt *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            od[db][i] *= alpha;
+            os[db][i] *= alpha;
+            ot[db][i] *= alpha;
+          }
+      }
+      // dense weights of the lane's 16 keys
+      float e[16], rs = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) e[v] = __builtin_amdgcn_exp2f(fmaf(s[v >> 2][v & 3], p.c, -m));
+      if (nval < RK) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (16 * (v >> 2) + g4 + (v & 3) >= nval) e[v] = 0.f;
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) rs += e[v];
+      ld += rs;
+      // B operands of the PV product: chunk c2 is e[8c2 .. 8c2 + 7]
+      uint32_t pd[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pd[k] = pack_bf16(e[2 * k], e[2 * k + 1]);
+      // masked weights: where every lane keeps all or none of its keys the
+      // mask zeroes whole packed words, else each weight
+      auto masked = [&](uint32_t lk, uint32_t* px, float& lx) __attribute__((always_inline)) {
+        if (!__builtin_amdgcn_ballot_w64(lk != 0u && lk != 0xFFFFu)) {
+          const uint32_t mk = lk ? ~0u : 0u;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) px[k] = pd[k] & mk;
+          lx += lk ? rs : 0.f;
+        } else {
+          float ex[16], sx = 0.f;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            ex[v] = __uint_as_float(__float_as_uint(e[v]) &
+                                    (uint32_t)__builtin_amdgcn_sbfe((int)lk, v, 1));
+            sx += ex[v];
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) px[k] = pack_bf16(ex[2 * k], ex[2 * k + 1]);
+          lx += sx;
+        }
+      };
+      uint32_t ps[8], pt[8];
+      masked(lane_keep(p, 1, fq, sq, key0, fk0, sk0, g4), ps, ls);
+      masked(lane_keep(p, 2, fq, sq, key0, fk0, sk0, g4), pt, lt);
+      // O^T += V^T P^T: V^T of dims 16db + n, positions 32c2 + 8g .. +7
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const bf16x8 bd = __builtin_bit_cast(
+            bf16x8, make_uint4(pd[4 * c2], pd[4 * c2 + 1], pd[4 * c2 + 2], pd[4 * c2 + 3]));
+        const bf16x8 bs = __builtin_bit_cast(
+            bf16x8, make_uint4(ps[4 * c2], ps[4 * c2 + 1], ps[4 * c2 + 2], ps[4 * c2 + 3]));
+        const bf16x8 bt = __builtin_bit_cast(
+            bf16x8, make_uint4(pt[4 * c2], pt[4 * c2 + 1], pt[4 * c2 + 2], pt[4 * c2 + 3]));
+        bf16x8 vb[NDB];  // the next 32 keys' fragments, read during these MFMAs
+        if (c2 == 0) {
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            vb[db] = *(const bf16x8*)(buf + KBYTES + (16 * db + n) * VROWB + 64 + 16 * g);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          od[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], bd, od[db], 0, 0, 0);
+          os[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], bs, os[db], 0, 0, 0);
+          ot[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], bt, ot[db], 0, 0, 0);
+        }
+        if (c2 == 0) {
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) va[db] = vb[db];
+        }
+      }
+    }
+    if (key0 + RK < k1) {
+      store(lds + ((it + 1) & 1) * STB);
+      if (key0 + 2 * RK < k1) fetch(key0 + 2 * RK);
+    }
+    __syncthreads();
+    sk0 += RK;
     while (sk0 >= p.S) {
       sk0 -= p.S;
       ++fk0;
     }
-    __syncthreads();  // every wave is done with the previous step's LDS
-    store();
-    __syncthreads();
-    if (key0 + RK < k1) fetch(key0 + RK);
-    // S^T = K Q^T for keys key0 .. key0+31 (rows past N clamped; masked)
-    f32x16 s;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 a = *(const bf16x8*)(lds + l32 * KROWB + 32 * ks + 16 * hl);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
-    }
-    // keep bits of the step's 32 keys under mask x (bit j: key key0 + j),
-    // then the lane's 16 (accumulator v: offset 16*(v/8) + 8hl + v%8)
-    const int nval = k1 - key0;
-    uint32_t keep = nval >= 32 ? ~0u : ((1u << nval) - 1u);
-    if (x != 0) keep &= mask_bits(p, x, fq, sq, fk0, sk0);
-    const uint32_t lk = ((keep >> (8 * hl)) & 0xFFu) | (((keep >> (16 + 8 * hl)) & 0xFFu) << 8);
-    // online softmax in log2 units
-    float mx = NEG_INF;
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-      if ((lk >> v) & 1u) mx = fmaxf(mx, s[v] * p.c);
-    {
-      float a, b;
-      halves(mx, a, b);
-      mx = fmaxf(a, b);
-    }
-    const float mn = fmaxf(m, mx);
-    const float alpha = mn == NEG_INF ? 1.f : __builtin_amdgcn_exp2f(m - mn);
-    float e[16], ls = 0.f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      e[v] = ((lk >> v) & 1u) ? __builtin_amdgcn_exp2f(s[v] * p.c - mn) : 0.f;
-      ls += e[v];
-    }
-    l = l * alpha + ls;
-    m = mn;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-    }
-    // O^T += V^T P^T: V^T of dims 32db + l32, keys 16kk + 8hl .. +7
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const uint4 w = make_uint4(pack_bf16(e[8 * kk + 0], e[8 * kk + 1]),
-                                 pack_bf16(e[8 * kk + 2], e[8 * kk + 3]),
-                                 pack_bf16(e[8 * kk + 4], e[8 * kk + 5]),
-                                 pack_bf16(e[8 * kk + 6], e[8 * kk + 7]));
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, w);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const bf16x8 vf = *(const bf16x8*)(lds + RK * KROWB + (32 * db + l32) * VROWB +
-                                           32 * kk + 16 * hl);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
-      }
-    }
   }
 
-  // (max, sum, O^T) of this split: O^T accumulator v of block db is dim
-  // 32db + 8(v/4) + 4hl + v%4 of row l32.
-  float lt;
-  {
-    float a, b;
-    halves(l, a, b);
-    lt = a + b;
-  }
+  // (max, sum, O^T) of this split for the three outputs: accumulator i of
+  // block db is dim 16db + 4g + i of row n.
+  ld = row_sum4(ld);
+  ls = row_sum4(ls);
+  lt = row_sum4(lt);
   if (!rvalid) return;
-  float* out = p.part + ((((size_t)h * p.n_rows + ri) * p.n_split + split) * 3 + x) * (D + 2);
-  if (hl == 0) {
+  float* out = p.part + (((size_t)h * p.n_rows + ri) * p.n_split + split) * 3 * (D + 2);
+  if (g == 0) {
     out[0] = m;
-    out[1] = lt;
+    out[1] = ld;
+    out[D + 2] = m;
+    out[D + 3] = ls;
+    out[2 * (D + 2)] = m;
+    out[2 * (D + 2) + 1] = lt;
   }
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) out[2 + 32 * db + 8 * (v >> 2) + 4 * hl + (v & 3)] = o[db][v];
+    for (int i = 0; i < 4; ++i) {
+      const int d = 2 + 16 * db + g4 + i;
+      out[d] = od[db][i];
+      out[D + 2 + d] = os[db][i];
+      out[2 * (D + 2) + d] = ot[db][i];
+    }
+}
+
+// Output x (1 spatial, 2 temporal) of sampled row t, computed directly:
+// the kept keys' scores in fp32, their maximum, then the normalised sum of
+// exp2(score - maximum) V. D threads; sh holds 2D floats. For rows whose
+// kept weights all fall far below the dense maximum (see kExactBelow).
+template <int D>
+__device__ float exact_output(const RouteParams& p, int h, int t, int x, float* sh) {
+  const int d = threadIdx.x;
+  const size_t hoff = (size_t)h * p.N * D;
+  const int fq = t / p.S, sq = t - fq * p.S;
+  __syncthreads();
+  sh[d] = bf16_to_f32(p.q[hoff + (size_t)t * D + d]);
+  __syncthreads();
+  auto kept = [&](int j) {
+    const int f = j / p.S, s = j - f * p.S;
+    const bool snk = p.sink && f == 0;
+    return x == 1 ? (abs(fq - f) <= p.W_f || snk) : (abs(sq - s) <= p.W_s || snk);
+  };
+  auto score = [&](int j) {
+    const uint16_t* kr = p.k + hoff + (size_t)j * D;
+    float acc = 0.f;
+    for (int i = 0; i < D; ++i) acc = fmaf(sh[i], bf16_to_f32(kr[i]), acc);
+    return acc * p.c;
+  };
+  float mx = -__builtin_huge_valf();
+  for (int j = d; j < p.N; j += D)
+    if (kept(j)) mx = fmaxf(mx, score(j));
+  sh[D + d] = mx;
+  __syncthreads();
+  for (int w = D / 2; w > 0; w >>= 1) {
+    if (d < w) sh[D + d] = fmaxf(sh[D + d], sh[D + d + w]);
+    __syncthreads();
+  }
+  mx = sh[D];
+  __syncthreads();
+  float o = 0.f, l = 0.f;
+  for (int base = 0; base < p.N; base += D) {
+    const int j = base + d;
+    sh[D + d] = (j < p.N && kept(j)) ? __builtin_amdgcn_exp2f(score(j) - mx) : 0.f;
+    __syncthreads();
+    const int cnt = min(D, p.N - base);
+    for (int jj = 0; jj < cnt; ++jj) {
+      const float wj = sh[D + jj];
+      l += wj;
+      o = fmaf(wj, bf16_to_f32(p.v[hoff + (size_t)(base + jj) * D + d]), o);
+    }
+    __syncthreads();
+  }
+  return o / l;
 }
 
 // One workgroup of D threads per (sampled row, head): merges the splits of
@@ -331,6 +511,7 @@ template <int D>
 __global__ __launch_bounds__(D) void route_rows(RouteParams p, double* row_err) {
   const int ri = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
   const float* base = p.part + ((size_t)h * p.n_rows + ri) * p.n_split * 3 * (D + 2);
+  __shared__ float sh[2 * D];
   float out[3];
 #pragma unroll
   for (int x = 0; x < 3; ++x) {
@@ -343,7 +524,9 @@ __global__ __launch_bounds__(D) void route_rows(RouteParams p, double* row_err) 
       L += b[1] * w;
       A += b[2 + d] * w;
     }
-    out[x] = L > 0.f ? A / L : 0.f;
+    // every thread holds the same L: the branch is uniform
+    if (x > 0 && !(L >= kExactBelow)) out[x] = exact_output<D>(p, h, p.rows[ri], x, sh);
+    else out[x] = L > 0.f ? A / L : 0.f;
   }
   __shared__ double red[2][D];
   red[0][d] = (double)(out[1] - out[0]) * (double)(out[1] - out[0]);
@@ -407,7 +590,7 @@ RouteLayout route_layout(int64_t N, int32_t H, int32_t D, int32_t n_rows, int32_
                          int64_t max_split) {
   RouteLayout L;
   L.pitch = (N + 63) / 64 * 64 + 64;  // a multiple of 64; keys past N read zeros
-  const int64_t pairs = ((n_rows + RQ - 1) / RQ + 1) / 2;  // workgroups per (head, split)
+  const int64_t pairs = ((n_rows + RQ - 1) / RQ + RW - 1) / RW;  // workgroups per (head, split)
   // Key splits. The time is about (rounds of resident workgroups) x (keys
   // per split), so take the split count that minimises rounds / splits, up
   // to about two rounds of workgroups (more splits cost partial results and
@@ -446,6 +629,7 @@ hipError_t launch_route(const void* q, const void* k, const void* v, char* scrat
   RouteParams p;
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
   p.vt = (const uint16_t*)(scratch + L.vt_off);
   p.rows = (const int32_t*)(scratch + L.rows_off);
   p.part = (float*)(scratch + L.part_off);
@@ -464,7 +648,8 @@ hipError_t launch_route(const void* q, const void* k, const void* v, char* scrat
   p.c = scale * 1.4426950408889634f;
   const int64_t total = (int64_t)H * (D / 8) * (L.pitch / 8);
   const dim3 vt_grid((unsigned)((total + 255) / 256));
-  const dim3 grid((unsigned)L.n_split, (unsigned)(((n_rows + RQ - 1) / RQ + 1) / 2), (unsigned)H);
+  const dim3 grid((unsigned)L.n_split, (unsigned)(((n_rows + RQ - 1) / RQ + RW - 1) / RW),
+                  (unsigned)H);
   double* row_err = (double*)(scratch + L.row_err_off);
   if (D == 128) {
     hipLaunchKernelGGL(vt_kernel<128>, vt_grid, dim3(256), 0, stream, (const uint4*)v,
@@ -520,7 +705,7 @@ RouteLayout route_static_layout(int64_t N, int32_t H, int32_t D, int32_t n_rows,
   // One head at a time: V^T, rows, partial results and row errors of one
   // head, then every head's (errors, kind); the key splits shrink until the
   // layout fits the array.
-  const int64_t kmax = (N + 31) / 32;
+  const int64_t kmax = (N + RK - 1) / RK;
   RouteLayout L = route_layout(N, 1, D, n_rows, slots, 0);
   for (int64_t ns = L.n_split; ns >= 1; --ns) {
     L = route_layout(N, 1, D, n_rows, slots, std::min(ns, kmax));

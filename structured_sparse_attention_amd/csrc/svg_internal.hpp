@@ -112,7 +112,7 @@ bool attn_supported(int32_t head_dim, int32_t tile_q, int32_t tile_k);
 // Scratch of one routing call (byte offsets into one allocation).
 struct RouteLayout {
   int64_t pitch;      // columns per V^T row
-  int64_t split_len;  // keys per split (a multiple of 32)
+  int64_t split_len;  // keys per split (a multiple of 64)
   int64_t n_split;
   int64_t vt_off, rows_off, part_off, row_err_off, err_off, kind_off, bytes;
 };

@@ -111,6 +111,37 @@ def test_planted_heads_route_to_their_masks():
     assert decided == 2
 
 
+def _far_maximum(w, j_star, seed):
+    """Every query scores 100 (natural log units) on key j_star and 0 on every
+    other key; V random. bf16-exact values."""
+    N, d = w.seq_len, w.head_dim
+    Q = np.zeros((1, N, d), np.float32)
+    K = np.zeros((1, N, d), np.float32)
+    Q[0, :, 0] = 100.0 * math.sqrt(d)
+    K[0, j_star, 0] = 1.0
+    V = np.random.default_rng(seed).standard_normal((1, N, d)).astype(np.float32)
+    return tuple(si.f32_to_bf16_bits(x) for x in (Q, K, V))
+
+
+@pytest.mark.parametrize("case", ["outside-both", "inside-temporal"])
+def test_far_maximum_outside_a_mask(case):
+    # The dense maximum (key j* = frame 5, raster index 40) lies 144 log2
+    # units above every other score. Rows in frames 0-3 never keep j* under
+    # the spatial mask (W_f = 1): that mask's weights, measured against the
+    # dense maximum, fall below fp32's normal range, and its output must be
+    # the plain average of its kept V rows all the same. Rows at raster
+    # indices 38-42 keep j* under the temporal mask (W_s = 2); rows at 0-30
+    # keep it under neither.
+    w = si.Workload("far-max", 6, 6, 8, ("spatial",), 64, 1, 2, True, 32, 32, False, seed=46)
+    S = w.tokens_per_frame
+    Q, K, V = _far_maximum(w, 5 * S + 40, 46)
+    cols = (38, 39, 40, 41, 42) if case == "inside-temporal" else (0, 7, 15, 22, 30)
+    rows = np.array([f * S + c for f in range(4) for c in cols])
+    say(f"[route-far-max] {case}: {len(rows)} rows")
+    kinds, decided = _compare(w, Q, K, V, rows, case,
+                              expect=["temporal"] if case == "inside-temporal" else None)
+
+
 def test_single_repeated_and_edge_rows():
     w = RAGGED
     Q, K, V = si.draw_qkv(w)
