@@ -293,11 +293,13 @@ svg_status svg_route_heads(const svg_mask_spec* spec, const void* q,
  * their partial results over at least one key split (n_rows x 3 x
  * (head_dim + 2) floats per split) and their row errors, plus 12 bytes per
  * head; at head_dim 128 a head of up to about 130,000 tokens fits with a
- * few thousand sampled rows. Every call on one GPU uses the same array: two
- * calls that overlap in time on one GPU (other host threads, other streams)
- * race and give wrong results; calls queued one after another are safe.
- * Nothing in the array needs clearing between calls: every value a call
- * reads, it has written. Synchronous, like svg_route_heads. */
+ * few thousand sampled rows. Every call on one GPU uses the same array;
+ * within a process the calls take a lock for their whole duration (they are
+ * synchronous), so calls from several host threads run one after another,
+ * on any GPU. Work that other code queues on the same GPU while a call runs
+ * does not touch the array. Nothing in the array needs clearing between
+ * calls: every value a call reads, it has written. Synchronous, like
+ * svg_route_heads. */
 svg_status svg_route_heads_noalloc(const svg_mask_spec* spec, const void* q,
                                    const void* k, const void* v,
                                    int32_t head_dim, float scale,

@@ -169,10 +169,21 @@ struct RouteParams {
 // S >= 64 the keys span at most two frames, split at relative key jb, and
 // each mask keeps a whole frame or one interval of it; shorter frames take
 // the key-by-key path.
+// sq_lo and sq_hi bound the raster indices of the wave's rows: where the
+// step lies in one frame and inside (or outside) every row's band, the
+// temporal bits are decided for the whole wave without per-lane work. (The
+// sampled rows are ordered by raster index, so a wave's band edges are close
+// together and most steps take that path.)
 __device__ __forceinline__ uint32_t lane_keep(const RouteParams& p, int x, int fq, int sq,
-                                              int key0, int fk0, int sk0, int g4) {
+                                              int key0, int fk0, int sk0, int g4, int sq_lo,
+                                              int sq_hi) {
   if (p.S >= RK) {
     const int jb = p.S - sk0;  // first key of frame fk0 + 1
+    if (x == 2 && jb >= RK) {
+      if (p.sink && fk0 == 0) return 0xFFFFu;
+      if (sk0 >= sq_hi - p.W_s && sk0 + RK - 1 <= sq_lo + p.W_s) return 0xFFFFu;
+      if (sk0 + RK - 1 < sq_lo - p.W_s || sk0 > sq_hi + p.W_s) return 0u;
+    }
     if (x == 1) {
       auto kept = [&](int f) { return abs(fq - f) <= p.W_f || (p.sink && f == 0); };
       const bool ka = kept(fk0);
@@ -226,8 +237,17 @@ __global__ __launch_bounds__(RW * 64) void route_partial(RouteParams p) {
   const bool wvalid = rb * RQ < p.n_rows;
   const int ri = rb * RQ + n;
   const bool rvalid = ri < p.n_rows;
-  const int t = rvalid ? p.rows[ri] : 0;
+  // lanes past the last row stand in for it (their results are not written)
+  const int t = p.rows[min(ri, p.n_rows - 1)];
   const int fq = t / p.S, sq = t - fq * p.S;
+  int sq_lo = sq, sq_hi = sq;  // over the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    sq_lo = min(sq_lo, __shfl_xor(sq_lo, o));
+    sq_hi = max(sq_hi, __shfl_xor(sq_hi, o));
+  }
+  sq_lo = __builtin_amdgcn_readfirstlane(sq_lo);
+  sq_hi = __builtin_amdgcn_readfirstlane(sq_hi);
   const size_t hoff = (size_t)h * p.N * D;
   // B operand of S^T: row n, dims 32kc + 8g .. +7
   bf16x8 qf[NKC];
@@ -388,8 +408,8 @@ __global__ __launch_bounds__(RW * 64) void route_partial(RouteParams p) {
         }
       };
       uint32_t ps[8], pt[8];
-      masked(lane_keep(p, 1, fq, sq, key0, fk0, sk0, g4), ps, ls);
-      masked(lane_keep(p, 2, fq, sq, key0, fk0, sk0, g4), pt, lt);
+      masked(lane_keep(p, 1, fq, sq, key0, fk0, sk0, g4, sq_lo, sq_hi), ps, ls);
+      masked(lane_keep(p, 2, fq, sq, key0, fk0, sk0, g4, sq_lo, sq_hi), pt, lt);
       // O^T += V^T P^T: V^T of dims 16db + n, positions 32c2 + 8g .. +7
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {

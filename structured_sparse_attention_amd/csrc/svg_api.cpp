@@ -4,10 +4,12 @@
 // thread-local message; nothing throws across the ABI.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -241,6 +243,23 @@ svg_status route_validate(const svg_mask_spec* spec, const void* q, const void* 
   out.W_s = spec->temporal_band < S ? spec->temporal_band : (int32_t)S;
   return SVG_OK;
 }
+
+// The sampled rows in the order the routing kernels take them: by raster
+// index (then by token), so that the 16 rows of a wave have neighbouring
+// temporal bands. A row's result does not depend on its place; only the
+// order of the float64 sum of row errors does.
+void order_rows(const int32_t* rows, int32_t n, int32_t S, int32_t* out) {
+  std::memcpy(out, rows, (size_t)n * 4);
+  std::sort(out, out + n, [S](int32_t a, int32_t b) {
+    const int32_t sa = a % S, sb = b % S;
+    return sa != sb ? sa < sb : a < b;
+  });
+}
+
+// Host staging of the ordered rows for svg_route_heads_noalloc; the lock
+// also serialises that call's use of the device scratch within a process.
+std::mutex g_noalloc_mu;
+int32_t g_noalloc_rows[65536];
 
 }  // namespace
 
@@ -675,7 +694,10 @@ svg_status svg_route_heads(const svg_mask_spec* spec, const void* q, const void*
   if (e != hipSuccess) return fail(SVG_ERR_OOM, "routing scratch of %lld bytes: %s",
                                    (long long)L.bytes, hipGetErrorString(e));
   std::vector<float> err_h((size_t)H * 2);
-  e = hipMemcpyAsync(scratch + L.rows_off, rows, (size_t)n_rows * 4, hipMemcpyHostToDevice, st);
+  std::vector<int32_t> ordered((size_t)n_rows);
+  order_rows(rows, n_rows, ra.S, ordered.data());
+  e = hipMemcpyAsync(scratch + L.rows_off, ordered.data(), (size_t)n_rows * 4,
+                     hipMemcpyHostToDevice, st);
   if (e == hipSuccess)
     e = svg::launch_route(q, k, v, scratch, L, ra.N, spec->frames, ra.S, H, head_dim, ra.W_f,
                           ra.W_s, spec->sink_first_frame ? 1 : 0, scale, n_rows, st);
@@ -713,7 +735,10 @@ svg_status svg_route_heads_noalloc(const svg_mask_spec* spec, const void* q, con
   hipError_t e = svg::route_static_scratch(&sc);
   if (e != hipSuccess) return hip_fail(e, "address of the routing scratch");
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  e = hipMemcpyAsync(sc + L.rows_off, rows, (size_t)n_rows * 4, hipMemcpyHostToDevice, st);
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  order_rows(rows, n_rows, ra.S, g_noalloc_rows);
+  e = hipMemcpyAsync(sc + L.rows_off, g_noalloc_rows, (size_t)n_rows * 4, hipMemcpyHostToDevice,
+                     st);
   if (e == hipSuccess)
     e = svg::launch_route_static(q, k, v, sc, L, res_off, ra.N, spec->frames, ra.S, H, head_dim,
                                  ra.W_f, ra.W_s, spec->sink_first_frame ? 1 : 0, scale, n_rows,
