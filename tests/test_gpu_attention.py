@@ -155,6 +155,29 @@ def test_full_size_sampled_rows(name):
     check(o[:, rows], ref, name)
 
 
+@pytest.mark.timeout(900)
+def test_largest_head_the_interface_takes():
+    # One spatial head of 4,095 frames of 64 x 64 tokens at d = 64:
+    # 16,773,120 tokens, 2,146,959,360 bytes per tensor, just under the 2 GiB
+    # per head that svg_attn_fwd accepts, with 1024 x 1024 tiles (a 268 MB
+    # class map). A byte offset or a key count that overflowed 32 bits would
+    # show here. The sampled rows include the first and the last token and
+    # frame edges; the oracle runs in this process (a forked pool would copy
+    # the widened keys and values into every worker).
+    w = si.Workload("largest-head", 4095, 64, 64, ("spatial",), 64, 0, 0, False, 1024, 1024,
+                    False, seed=48)
+    N, S = w.seq_len, w.tokens_per_frame
+    assert N * w.head_dim * 2 < 2 ** 31 <= (N + S) * w.head_dim * 2
+    say(f"[attn-largest] N={N} d={w.head_dim} tiles {w.tile_q}x{w.tile_k}")
+    Q, K, V = si.draw_qkv(w)
+    say("  inputs drawn")
+    o = run_attention(w, Q, K, V)
+    say("  attention done")
+    rows = np.unique(np.array([0, 1, S - 1, S, N // 2, N - S - 1, N - S, N - 2, N - 1]))
+    ref = oracle_rows(w, Q, K, V, masks_of(w), rows, jobs=1)
+    check(o[:, rows], ref, "largest head")
+
+
 @pytest.mark.parametrize("name", ["d128-split", "d64-split-bq32"])
 def test_launch_plan_cuts_rows_of_the_split_shapes(name):
     # the shapes above exist to exercise cut rows: make sure the plan cuts
