@@ -114,9 +114,15 @@ typedef struct svg_mask_spec {
   int32_t round_mode;        /* svg_round_mode                               */
 } svg_mask_spec;
 
-/* Opaque, device-resident tile map. Read-only after it is built; one map may
- * serve any number of svg_attn_fwd calls, on any stream of the same device,
- * once the build has completed on the stream it was queued on. */
+/* Opaque, device-resident tile map. One map may serve any number of
+ * svg_attn_fwd calls, on any streams of the device it was built on. Its
+ * uses share the map's workspace (schedule, launch plan, partial results of
+ * cut rows), so the library orders them on the device in the order the
+ * calls are made: each svg_attn_fwd and svg_tile_map_rebuild waits on its
+ * stream, without blocking the host, for the map's last build and last
+ * attention launch. Under stream capture these waits are skipped (an event
+ * recorded outside a capture cannot be waited for inside it) and the caller
+ * orders the uses of one map. */
 typedef struct svg_tile_map svg_tile_map;
 
 typedef struct svg_tile_map_info {
@@ -209,7 +215,8 @@ svg_status svg_tile_map_copy_schedule(const svg_tile_map* map, int32_t* row_ptr,
  * INVALID_ARG (null pointers), HIP. */
 svg_status svg_tile_map_plan_info(const svg_tile_map* map, svg_plan_info* out);
 
-/* Free a map (NULL is accepted). Waits for work queued on its build stream. */
+/* Free a map (NULL is accepted). Waits for its last build and its last
+ * attention launch. */
 svg_status svg_tile_map_destroy(svg_tile_map* map);
 
 /* A5-A8: O = softmax(scale * Q K^T masked to M) V for every head.

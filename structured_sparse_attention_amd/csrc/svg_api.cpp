@@ -67,6 +67,7 @@ void free_plan(svg_tile_map* m) {
 // Everything a map owns; the caller has waited for its queued work.
 void free_map(svg_tile_map* m) {
   if (m->built) (void)hipEventDestroy(m->built);
+  if (m->used) (void)hipEventDestroy(m->used);
   free_plan(m);
   free_buffers(m->buf);
   delete m;
@@ -186,6 +187,23 @@ svg_status check_device(const svg_tile_map* m) {
     return fail(SVG_ERR_INVALID_ARG, "the map was built on device %d, the current device is %d",
                 m->device, dev);
   return SVG_OK;
+}
+
+// Uses of one map are ordered on the device, since they share its workspace
+// (schedule, plan, partial results): on `st`, without blocking the host, wait
+// for the map's last build and, unless `after_build_only`, its last attention
+// launch. Under stream capture nothing is waited for (an event recorded
+// outside a capture cannot be waited for inside it): the caller orders them.
+hipError_t order_after(const svg_tile_map* m, hipStream_t st, bool after_build_only,
+                       bool& capturing) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(st, &cs);
+  if (e != hipSuccess) return e;
+  capturing = cs != hipStreamCaptureStatusNone;
+  if (capturing) return hipSuccess;
+  if (!after_build_only && m->used_valid) e = hipStreamWaitEvent(st, m->used, 0);
+  if (e == hipSuccess && m->built) e = hipStreamWaitEvent(st, m->built, 0);
+  return e;
 }
 
 svg_status run_build(svg_tile_map* m, hipStream_t stream) {
@@ -392,6 +410,11 @@ svg_status svg_build_tile_map(const svg_mask_spec* spec, int32_t tile_q, int32_t
     free_map(m);
     return hip_fail(e, "hipEventCreate");
   }
+  if ((e = hipEventCreateWithFlags(&m->used, hipEventDisableTiming)) != hipSuccess) {
+    m->used = nullptr;
+    free_map(m);
+    return hip_fail(e, "hipEventCreate");
+  }
   // Queued on the caller's stream, nothing waited for: head kinds from
   // kernel arguments, the tile-map kernels, the row info to the pinned
   // staging, the planning host function, the plan image to the device.
@@ -433,7 +456,17 @@ svg_status svg_tile_map_rebuild(svg_tile_map* map, void* stream) {
   if (!map) return fail(SVG_ERR_INVALID_ARG, "map is NULL");
   const svg_status s = check_device(map);
   if (s != SVG_OK) return s;
-  return run_build(map, reinterpret_cast<hipStream_t>(stream));
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(map->mu);
+  hipError_t e = hipSuccess;
+  if (map->used_valid) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(st, &cs);
+    if (e == hipSuccess && cs == hipStreamCaptureStatusNone)
+      e = hipStreamWaitEvent(st, map->used, 0);
+  }
+  if (e != hipSuccess) return hip_fail(e, "ordering after the map's last attention launch");
+  return run_build(map, st);
 }
 
 svg_status svg_tile_map_info_get(const svg_tile_map* map, svg_tile_map_info* out) {
@@ -535,6 +568,11 @@ svg_status svg_tile_map_plan_info(const svg_tile_map* map, svg_plan_info* out) {
 svg_status svg_tile_map_destroy(svg_tile_map* map) {
   if (!map) return ok();
   svg_status s = wait_built(map);
+  if (s == SVG_OK && map->used_valid) {
+    // the last attention launch that used the map, on whatever stream
+    const hipError_t e = hipEventSynchronize(map->used);
+    if (e != hipSuccess) s = hip_fail(e, "hipEventSynchronize");
+  }
   free_map(map);
   return s == SVG_OK ? ok() : s;
 }
@@ -578,10 +616,19 @@ svg_status svg_attn_fwd(const void* q, const void* k, const void* v, void* o, in
   const svg_status ds = check_device(map);
   if (ds != SVG_OK) return ds;
   svg::AttnArgs a{q, k, v, o, head_dim, scale, flags};
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(map->mu);
+  bool capturing = false;
+  hipError_t e = order_after(map, st, false, capturing);
+  if (e != hipSuccess) return hip_fail(e, "ordering after the map's last use");
   const uint32_t ring = map->launches.fetch_add(1, std::memory_order_relaxed) % svg::kQueueRing;
-  const hipError_t e = svg::launch_attn_fwd(g, map->buf, map->plan, ring, a,
-                                            reinterpret_cast<hipStream_t>(stream));
+  e = svg::launch_attn_fwd(g, map->buf, map->plan, ring, a, st);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  if (!capturing) {
+    e = hipEventRecord(map->used, st);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    map->used_valid = true;
+  }
   return ok();
 }
 

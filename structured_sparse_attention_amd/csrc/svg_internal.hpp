@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "svg_attn.h"
@@ -177,4 +178,9 @@ struct svg_tile_map {
   int device = 0;
   hipEvent_t built = nullptr;  // recorded after every (re)build
   mutable std::atomic<uint32_t> launches{0};  // picks each launch's queue counters
+  // Uses of the map are ordered on the device (they share its workspace):
+  // `used` is recorded after every attention launch outside stream capture.
+  hipEvent_t used = nullptr;
+  mutable bool used_valid = false;
+  mutable std::mutex mu;
 };

@@ -371,3 +371,34 @@ def test_repeated_calls_are_deterministic():
     b = run_attention(w, Q, K, V, tile_map=tm)
     np.testing.assert_array_equal(a, b)
     tm.destroy()
+
+
+def test_one_map_serves_two_streams():
+    # Launches that share one map, queued on two streams with nothing between
+    # them: they share the map's workspace, so the library orders them on the
+    # device and each output equals the one its inputs give alone. The shape
+    # cuts rows, so every launch writes and merges partial results.
+    import torch
+    w = next(x for x in SMALL if x.name == "d128-split")
+    tm = build_map(w)
+    assert tm.plan_info()["partial_slots"] > 0
+    sets = [inputs(w), si.draw_qkv(w, seed=w.seed + 1000)]
+    dev = [[to_kernel_layout(w, to_device(x)) for x in qkv] for qkv in sets]
+    torch.cuda.synchronize()
+    alone = []
+    for q, k, v in dev:
+        o = torch.empty_like(q)
+        svg.svg_attn_fwd(q, k, v, o, w.head_kinds, tm)
+        torch.cuda.synchronize()
+        alone.append(o)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(dev[0][0]) for _ in dev]
+    torch.cuda.synchronize()
+    for rep in range(4):
+        say(f"[attn-two-streams] round {rep}")
+        for (q, k, v), o, st in zip(dev, outs, streams):
+            svg.svg_attn_fwd(q, k, v, o, w.head_kinds, tm, stream=st)
+        torch.cuda.synchronize()
+        for o, a in zip(outs, alone):
+            assert torch.equal(o, a)
+    tm.destroy()
