@@ -161,17 +161,20 @@ typedef struct svg_plan_info {
 /* A3+A4: classify every tile of every head and compact, per (head, Q tile),
  * the KV tiles to execute: FULL ids ascending, then BOUNDARY ids ascending,
  * plus the temporal sink split (a, b). Then plan the attention launch: one
- * workgroup per compute unit, each with a fixed list of work items (a range
- * of 64-key steps of a workgroup-sized slice of a schedule row); the slices
- * an XCD works on at one time are neighbouring Q tiles, and the last slices
- * of each XCD's share are cut between its workgroups so that all of them
- * end together. The plan is computed on the host from the map's row counts
- * by a host function queued on `stream` and then copied to the device.
- * Everything is queued on `stream` and the call returns without waiting.
- * Allocates the map's device buffers (class map, schedule, plan, and up to
- * 2 x (compute units) partial results of (query rows of a workgroup) x 128
- * fp32 values for cut slices: 64 MiB for 256-row workgroups on 256 compute
- * units) and pinned host staging, all freed by svg_tile_map_destroy.
+ * workgroup per compute unit, taking work items (a range of 64-key steps of
+ * a workgroup-sized slice of a schedule row) from its XCD's queue and then
+ * from a tail queue shared by all XCDs. The slices an XCD works on at one
+ * time are neighbouring Q tiles; the last slices of each XCD's share are
+ * cut between its workgroups so that they end together; the tail (about 5%
+ * of the work, in parts that shrink towards its end) evens out XCDs that
+ * run at different speeds. The plan is computed on the host from the map's
+ * row counts by a host function queued on `stream` and then copied to the
+ * device. Everything is queued on `stream` and the call returns without
+ * waiting. Allocates the map's device buffers (class map, schedule, plan,
+ * and up to 5 x (compute units) partial results of (query rows of a
+ * workgroup) x 128 fp32 values for cut slices: 160 MiB for 256-row
+ * workgroups on 256 compute units) and pinned host staging, all freed by
+ * svg_tile_map_destroy.
  * Supported tile sizes: tile_q in {32, 64, 128} or a multiple of 256 up to
  * 2^20; tile_k a multiple of 32 in [32, 1024].
  * Errors: INVALID_ARG (null spec/out/head_kind, bad sizes or kinds),

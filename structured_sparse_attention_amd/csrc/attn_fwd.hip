@@ -46,13 +46,15 @@
 // per-lane address arithmetic and rows past the sequence read as zeros.
 //
 // Dispatch. The launch is persistent: one workgroup per compute unit, each
-// walking the list of work items that the map's plan gave it (plan.hpp): a
-// work item is a range of steps of one workgroup-sized slice of a schedule
-// row. The plan keeps the Q tiles an XCD works on at one time neighbours
-// (they share their KV tiles in its L2) and ends every workgroup level by
-// cutting the last rows of each XCD's band between workgroups. A cut row's
-// parts write their unnormalised O, running maximum and row sum to partial
-// slots, and combine_kernel merges them after the launch.
+// taking work items from its XCD's queue of the map's plan (plan.hpp), and
+// then from a tail shared by all XCDs: a work item is a range of steps of
+// one workgroup-sized slice of a schedule row. The plan keeps the Q tiles an
+// XCD works on at one time neighbours (they share their KV tiles in its L2)
+// and ends the XCD's workgroups level by cutting its last rows between them;
+// the shared tail, cut into parts that shrink towards its end, evens out
+// XCDs that run at different speeds. A cut row's parts write their
+// unnormalised O, running maximum and row sum to partial slots, and
+// combine_kernel merges them after the launch.
 #include "svg_internal.hpp"
 
 #include <math.h>
@@ -108,9 +110,9 @@ struct KParams {
   int32_t N, F, S, W_f, W_s, sink;
   int32_t BQ, BK, nQ, nsub, cpt;
   const int32_t* entries;
-  const int32_t* item_ptr;  // per-XCD queue bounds [n_xcd + 1]
+  const int32_t* item_ptr;  // queue bounds [n_xcd + 2]: XCD x's queue, then the shared tail
   const int4* items;        // ItemDesc, three int4 each (see svg_internal.hpp)
-  int32_t* counters;        // this launch's queue positions [n_xcd], zeroed
+  int32_t* counters;        // this launch's queue positions [n_xcd + 1], zeroed
   int32_t n_xcd;
   // bounds every plan entry is checked against
   int32_t H, n_units, max_items, max_slots, n_k_tiles, entry_cap;
@@ -460,15 +462,28 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(KParams p) {
   // and roughly when; the queue lets the workgroups that really finish
   // first take the next item, so that neighbouring Q tiles keep running
   // together and share their KV tiles in the L2.
-  __shared__ int s_take;
+  // Once the XCD's queue is empty, the workgroup takes items from the
+  // shared tail (queue n_xcd), whose parts shrink towards its end: XCDs do
+  // not run equally fast, and the tail lets the faster ones take more.
+  __shared__ int s_take, s_queue;
   uint32_t xcc = __builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 20) & 0xF;  // XCC_ID
   if ((int)xcc >= p.n_xcd) xcc = blockIdx.x % p.n_xcd;
-  const int q_begin = max(0, p.item_ptr[xcc]);
-  const int q_end = min(p.item_ptr[xcc + 1], p.max_items);
+  int queue = xcc;  // (thread 0's copy decides)
   for (;;) {
     __syncthreads();  // every wave has read the previous position
-    if (threadIdx.x == 0) s_take = atomicAdd(p.counters + xcc, 1);
+    if (threadIdx.x == 0) {
+      int t = atomicAdd(p.counters + queue, 1);
+      if (queue != p.n_xcd && t >= p.item_ptr[queue + 1] - p.item_ptr[queue]) {
+        queue = p.n_xcd;
+        t = atomicAdd(p.counters + queue, 1);
+      }
+      s_take = t;
+      s_queue = queue;
+    }
     __syncthreads();
+    const int qs = __builtin_amdgcn_readfirstlane(s_queue);
+    const int q_begin = max(0, p.item_ptr[qs]);
+    const int q_end = min(p.item_ptr[qs + 1], p.max_items);
     const int it = q_begin + __builtin_amdgcn_readfirstlane(s_take);
     if (it >= q_end) break;
     // the item and its row: (unit, first step, end step, partial slot),
@@ -961,27 +976,29 @@ __global__ __launch_bounds__(64) void zero_counters_kernel(int32_t* c, int32_t n
 }
 
 template <int D, int NW>
-hipError_t launch(const KParams& kp, const CombineParams& cp, int n_wg, hipStream_t stream) {
-  hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, stream, kp.counters, kp.n_xcd);
+hipError_t launch(const KParams& kp, const CombineParams& cp, int n_wg, int n_combine,
+                  hipStream_t stream) {
+  hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, stream, kp.counters,
+                     kp.n_xcd + 1);
   hipError_t e0 = hipGetLastError();
   if (e0 != hipSuccess) return e0;
   hipLaunchKernelGGL((attn_fwd_kernel<D, NW>), dim3(n_wg), dim3(NW * 64), 0, stream, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int RB = NW * QW < CRB ? NW * QW : CRB;
-  hipLaunchKernelGGL((combine_kernel<D, NW * QW>), dim3(n_wg * (NW * QW / RB)), dim3(256), 0,
-                     stream, cp);
+  hipLaunchKernelGGL((combine_kernel<D, NW * QW>), dim3(n_combine * (NW * QW / RB)), dim3(256),
+                     0, stream, cp);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(int nw, const KParams& kp, const CombineParams& cp, int n_wg,
+hipError_t launch_d(int nw, const KParams& kp, const CombineParams& cp, int n_wg, int n_combine,
                     hipStream_t stream) {
   switch (nw) {
-    case 8: return launch<D, 8>(kp, cp, n_wg, stream);
-    case 4: return launch<D, 4>(kp, cp, n_wg, stream);
-    case 2: return launch<D, 2>(kp, cp, n_wg, stream);
-    default: return launch<D, 1>(kp, cp, n_wg, stream);
+    case 8: return launch<D, 8>(kp, cp, n_wg, n_combine, stream);
+    case 4: return launch<D, 4>(kp, cp, n_wg, n_combine, stream);
+    case 2: return launch<D, 2>(kp, cp, n_wg, n_combine, stream);
+    default: return launch<D, 1>(kp, cp, n_wg, n_combine, stream);
   }
 }
 
@@ -1018,7 +1035,7 @@ hipError_t launch_attn_fwd(const MapGeometry& g, const MapBuffers& b, const Plan
   kp.cpt = (g.BK + CK - 1) / CK;
   kp.entries = b.entries;
   kp.item_ptr = pl.dev + 4;
-  kp.counters = pl.counters + (size_t)(ring % kQueueRing) * pl.n_xcd;
+  kp.counters = pl.counters + (size_t)(ring % kQueueRing) * (pl.n_xcd + 1);
   kp.n_xcd = pl.n_xcd;
   kp.items = (const int4*)(pl.dev + pl.items_off());
   kp.H = g.H;
@@ -1046,8 +1063,9 @@ hipError_t launch_attn_fwd(const MapGeometry& g, const MapBuffers& b, const Plan
   cp.n_units = kp.n_units;
   cp.max_slots = kp.max_slots;
   cp.c = kp.c;
-  return a.head_dim == 128 ? launch_d<128>(nw, kp, cp, pl.n_wg, stream)
-                           : launch_d<64>(nw, kp, cp, pl.n_wg, stream);
+  const int n_combine = (int)pl.max_combine;
+  return a.head_dim == 128 ? launch_d<128>(nw, kp, cp, pl.n_wg, n_combine, stream)
+                           : launch_d<64>(nw, kp, cp, pl.n_wg, n_combine, stream);
 }
 
 }  // namespace svg

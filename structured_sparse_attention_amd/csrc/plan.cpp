@@ -11,7 +11,7 @@ namespace svg {
 
 void plan_persistent(const int32_t* steps, const float* weight, int32_t n_units, int32_t n_wg,
                      int32_t n_xcd, int32_t block, int32_t overhead, int32_t min_part,
-                     PlanResult& out) {
+                     double tail, PlanResult& out) {
   out = PlanResult{};
   const int32_t P = std::max(1, n_wg);
   const int32_t X = std::max(1, std::min(n_xcd, P));
@@ -37,6 +37,16 @@ void plan_persistent(const int32_t* steps, const float* weight, int32_t n_units,
   for (int64_t j = 0; j < M; ++j) pre[j + 1] = pre[j] + cost(j);
   const double total = pre[M];
 
+  // The shared tail: the last units, whose cost is at most `tail` of the
+  // total (at most P units), kept when there are four units per workgroup.
+  // The XCDs share units [0, Mx) as below.
+  int64_t Mx = M;
+  if (tail > 0.0 && M >= 4 * (int64_t)P) {
+    const double want = tail * total;
+    while (Mx > 0 && M - Mx < P && pre[M] - pre[Mx - 1] <= want) --Mx;
+  }
+  const double xtotal = pre[Mx];
+
   // Workgroups of XCD x: i = k * X + x for k < G[x].
   std::vector<int32_t> G(X);
   for (int32_t x = 0; x < X; ++x) G[x] = P / X + (x < P % X ? 1 : 0);
@@ -52,7 +62,7 @@ void plan_persistent(const int32_t* steps, const float* weight, int32_t n_units,
     std::vector<double> have(X, 0.0);
     int64_t rest = 0;
     if (block > 0) {
-      const int64_t nb = (M + block - 1) / block;
+      const int64_t nb = (Mx + block - 1) / block;
       const int64_t rounds = std::max<int64_t>(0, nb / X - 1);
       for (int64_t r = 0; r < rounds; ++r)
         for (int32_t x = 0; x < X; ++x)
@@ -67,16 +77,16 @@ void plan_persistent(const int32_t* steps, const float* weight, int32_t n_units,
     std::vector<double> need(X);
     double sneed = 0.0;
     for (int32_t x = 0; x < X; ++x) {
-      need[x] = std::max(0.0, total * (double)G[x] / (double)P - have[x]);
+      need[x] = std::max(0.0, xtotal * (double)G[x] / (double)P - have[x]);
       sneed += need[x];
     }
-    const double rcost = total - pre[rest];
+    const double rcost = xtotal - pre[rest];
     double acc = pre[rest];
     int64_t j = rest;
     for (int32_t x = 0; x < X; ++x) {
       acc += sneed > 0.0 ? rcost * need[x] / sneed : rcost / X;
       // a unit goes to the run its cost midpoint falls in
-      while (j < M && (x == X - 1 || pre[j] + 0.5 * cost(j) < acc)) seq[x].push_back(j++);
+      while (j < Mx && (x == X - 1 || pre[j] + 0.5 * cost(j) < acc)) seq[x].push_back(j++);
     }
   }
 
@@ -190,17 +200,9 @@ void plan_persistent(const int32_t* steps, const float* weight, int32_t n_units,
     }
   }
 
-  out.n_slots = next_slot;
-  out.item_ptr.assign(P + 1, 0);
-  for (int32_t i = 0; i < P; ++i) {
-    out.item_ptr[i + 1] = out.item_ptr[i] + (int32_t)per_wg[i].size();
-    out.items.insert(out.items.end(), per_wg[i].begin(), per_wg[i].end());
-    out.max_load = std::max(out.max_load, (int64_t)std::llround(load[i]));
-    out.total_load += (int64_t)std::llround(load[i]);
-  }
   // per XCD: its workgroups' items by simulated start (then workgroup and
   // position, for a fixed order)
-  out.queue_ptr.assign(X + 1, 0);
+  out.queue_ptr.assign(X + 2, 0);
   for (int32_t x = 0; x < X; ++x) {
     struct Q {
       double start;
@@ -214,6 +216,94 @@ void plan_persistent(const int32_t* steps, const float* weight, int32_t n_units,
     });
     for (const Q& e : q) out.queue_items.push_back(per_wg[e.wg][e.pos]);
     out.queue_ptr[x + 1] = (int32_t)out.queue_items.size();
+  }
+
+  // The tail: each unit cut, in sequence order, into parts of about the
+  // tail work left over the workgroups (at least mp steps; a rest shorter
+  // than that joins the part before it), so that the parts shrink towards
+  // the end; mp is min_part, raised where the parts would need more than the
+  // tail's slots. The queue takes them longest first.
+  {
+    double tail_work = 0.0;
+    int32_t longest = 0;
+    for (int64_t j = Mx; j < M; ++j) {
+      tail_work += work(j);
+      longest = std::max(longest, steps[U[j]]);
+    }
+    const int64_t budget = (int64_t)kPlanTailSlotsPerWg * P;
+    // parts of tail unit j, given the tail work r left before it
+    auto cut = [&](int64_t j, double r, int32_t mp, std::vector<std::pair<int32_t, int32_t>>& parts) {
+      const int32_t n = steps[U[j]];
+      const double wj = w(j);
+      parts.clear();
+      for (int32_t s0 = 0; s0 < n;) {
+        const double want = std::ceil(r / ((double)P * wj));
+        int32_t len = (int32_t)std::min<double>(n - s0, std::max<double>(mp, want));
+        if (n - s0 - len < mp) len = n - s0;
+        parts.emplace_back(s0, s0 + len);
+        s0 += len;
+        r -= wj * len;
+      }
+    };
+    std::vector<std::pair<int32_t, int32_t>> parts;  // [s0, e)
+    auto slots_for = [&](int32_t mp) {
+      int64_t n = 0;
+      double r = tail_work;
+      for (int64_t j = Mx; j < M; ++j) {
+        cut(j, r, mp, parts);
+        if (parts.size() > 1) n += (int64_t)parts.size();
+        r -= work(j);
+      }
+      return n;
+    };
+    int32_t mp = std::max(1, min_part);
+    while (mp <= longest && slots_for(mp) > budget) mp += std::max(1, mp / 8);
+    std::vector<std::pair<PlanItem, double>> titems;  // item, cost
+    double rem = tail_work;
+    for (int64_t j = Mx; j < M; ++j) {
+      const int32_t unit = U[j], n = steps[unit];
+      const double wj = w(j);
+      cut(j, rem, mp, parts);
+      rem -= work(j);
+      if (parts.size() <= 1) {
+        titems.emplace_back(PlanItem{unit, 0, kPlanToEnd, -1}, wj * n + overhead);
+      } else {
+        out.combine.push_back(PlanCombine{unit, next_slot, (int32_t)parts.size(), 0});
+        for (size_t i = 0; i < parts.size(); ++i) {
+          const int32_t s1 = i + 1 < parts.size() ? parts[i].second : kPlanToEnd;
+          titems.emplace_back(PlanItem{unit, parts[i].first, s1, next_slot++},
+                              wj * (parts[i].second - parts[i].first) + overhead);
+        }
+      }
+    }
+    // longest first (stable), so that a rest joined to a part does not
+    // come last
+    std::stable_sort(titems.begin(), titems.end(),
+                     [](const std::pair<PlanItem, double>& a, const std::pair<PlanItem, double>& b) {
+                       return a.second > b.second;
+                     });
+    // queue X; for the statistics, each part goes to the workgroup that is
+    // free first by the cost model
+    typedef std::pair<double, int32_t> Slot;
+    std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> freeq;
+    for (int32_t i = 0; i < P; ++i) freeq.push(Slot(load[i], i));
+    for (const auto& ti : titems) {
+      out.queue_items.push_back(ti.first);
+      const Slot f = freeq.top();
+      freeq.pop();
+      emit(f.second, ti.first, ti.second);
+      freeq.push(Slot(load[f.second], f.second));
+    }
+    out.queue_ptr[X + 1] = (int32_t)out.queue_items.size();
+  }
+
+  out.n_slots = next_slot;
+  out.item_ptr.assign(P + 1, 0);
+  for (int32_t i = 0; i < P; ++i) {
+    out.item_ptr[i + 1] = out.item_ptr[i] + (int32_t)per_wg[i].size();
+    out.items.insert(out.items.end(), per_wg[i].begin(), per_wg[i].end());
+    out.max_load = std::max(out.max_load, (int64_t)std::llround(load[i]));
+    out.total_load += (int64_t)std::llround(load[i]);
   }
 }
 

@@ -11,6 +11,7 @@
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <stdexcept>
 #include <string>
 #include <vector>
 
@@ -130,7 +131,14 @@ void plan_host_fn(void* user) {
       weight[u] = svg::kPlanStepWeight[j.kinds[(u / j.nsub) / g.nQ]];
     svg::PlanResult r;
     svg::plan_persistent(steps.data(), weight.data(), (int32_t)steps.size(), pl.n_wg, pl.n_xcd,
-                         svg::kPlanBlockUnits, svg::kPlanItemOverhead, svg::kPlanMinPart, r);
+                         svg::kPlanBlockUnits, svg::kPlanItemOverhead, svg::kPlanMinPart,
+                         svg::kPlanTail, r);
+    // (the staging holds the bounds the plan keeps; a plan past them would
+    // be a planner fault, and falls back to the plan below)
+    if ((int64_t)r.queue_items.size() > pl.max_items || r.n_slots > pl.max_slots ||
+        (int64_t)r.combine.size() > pl.max_combine ||
+        (int64_t)r.queue_ptr.size() != pl.n_xcd + 2)
+      throw std::length_error("launch plan past its bounds");
     im[0] = (int32_t)r.items.size();
     im[1] = (int32_t)r.combine.size();
     im[2] = r.n_slots;
@@ -156,7 +164,7 @@ void plan_host_fn(void* user) {
         if (((u / j.nsub) % g.nQ) * (int64_t)g.BQ + (u % j.nsub) * (int64_t)j.wgq < g.N)
           items[n++] = desc((int32_t)u, 0, svg::kPlanToEnd, -1);
     }
-    ptr[pl.n_xcd] = n;
+    ptr[pl.n_xcd] = ptr[pl.n_xcd + 1] = n;  // an empty shared tail
     im[0] = n;
     im[1] = im[2] = im[3] = 0;
     j.items = n;
@@ -378,6 +386,7 @@ svg_status svg_build_tile_map(const svg_mask_spec* spec, int32_t tile_q, int32_t
   }
   pl.max_items = svg::plan_max_items(n_units, pl.n_wg);
   pl.max_slots = svg::plan_max_slots(pl.n_wg);
+  pl.max_combine = svg::plan_max_combine(pl.n_wg);
   const int64_t part_rows = pl.max_slots * job.wgq;
   hipError_t ea = hipSuccess;
   auto step = [&](hipError_t x) { if (ea == hipSuccess) ea = x; };
@@ -389,7 +398,7 @@ svg_status svg_build_tile_map(const svg_mask_spec* spec, int32_t tile_q, int32_t
   step(alloc(&b.rowstats, R * svg::kRowStats));
   step(alloc(&b.stats, (int64_t)g.H * svg::kRowStats));
   step(alloc(&pl.dev, pl.dev_ints()));
-  step(alloc(&pl.counters, (int64_t)svg::kQueueRing * pl.n_xcd));
+  step(alloc(&pl.counters, (int64_t)svg::kQueueRing * (pl.n_xcd + 1)));
   step(alloc(&pl.part_o, part_rows * svg::kAttnMaxHeadDim));
   step(alloc(&pl.part_ml, part_rows * 2));
   if (ea == hipSuccess)

@@ -67,23 +67,24 @@ static_assert(sizeof(ItemDesc) == 48, "three 16-byte loads");
 
 // Work plan of the persistent attention launch (plan.hpp), device side.
 // `dev` holds, as int32: a header [n_items, n_combine, n_slots, 0], then
-// the per-XCD queue bounds queue_ptr [n_xcd + 1] in a field of n_wg + 1
-// entries padded to a multiple of 4, then max_items ItemDesc (12 int32
-// each, XCD by XCD in queue order) and n_wg combine entries (PlanCombine,
-// 4 int32 each). `counters` is a ring of kQueueRing sets of n_xcd queue
-// positions; every launch takes the next set and zeroes it first.
+// the queue bounds queue_ptr [n_xcd + 2] (queue x < n_xcd: XCD x's items;
+// queue n_xcd: the shared tail) in a field of n_wg + 2 entries padded to a
+// multiple of 4, then max_items ItemDesc (12 int32 each, queue by queue in
+// queue order) and max_combine combine entries (PlanCombine, 4 int32 each).
+// `counters` is a ring of kQueueRing sets of n_xcd + 1 queue positions;
+// every launch takes the next set and zeroes it first.
 constexpr int32_t kQueueRing = 256;
 struct PlanBuffers {
   int32_t* dev = nullptr;
-  int32_t* counters = nullptr;  // [kQueueRing][n_xcd]
+  int32_t* counters = nullptr;  // [kQueueRing][n_xcd + 1]
   float* part_o = nullptr;  // [max_slots][rows of a workgroup][128]
   float* part_ml = nullptr; // [max_slots][rows of a workgroup][2]
   int32_t n_wg = 0, n_xcd = 0;
-  int64_t max_items = 0, max_slots = 0;
-  int64_t ptr_ints() const { return (n_wg + 1 + 3) / 4 * 4; }
+  int64_t max_items = 0, max_slots = 0, max_combine = 0;
+  int64_t ptr_ints() const { return (n_wg + 2 + 3) / 4 * 4; }
   int64_t items_off() const { return 4 + ptr_ints(); }
   int64_t combine_off() const { return items_off() + 12 * max_items; }
-  int64_t dev_ints() const { return combine_off() + 4 * (int64_t)n_wg; }
+  int64_t dev_ints() const { return combine_off() + 4 * max_combine; }
 };
 
 // Query rows per workgroup (32 per wave) of the attention kernel for a Q
@@ -98,6 +99,11 @@ constexpr int32_t kPlanItemOverhead = 4;
 constexpr int32_t kPlanMinPart = 32;
 // Work units per block dealt to the XCDs in rounds (plan_persistent).
 constexpr int32_t kPlanBlockUnits = 32;
+// Share of the work kept for the shared tail of the launch (plan_persistent):
+// enough to absorb XCDs that run about 5% apart (measured on MI355X: 3-6%
+// between the fastest and the slowest XCD of a chip; 4% and 7% measured
+// alike on the main workload).
+constexpr double kPlanTail = 0.05;
 // Relative cost of a 64-key step by head kind (spatial, temporal, dense),
 // measured on the main workload's shape with the same kernel.
 constexpr float kPlanStepWeight[3] = {1.030f, 1.000f, 0.985f};

@@ -197,7 +197,8 @@ def test_main_launch_plan_is_level():
     mean = info["total_load"] / info["workgroups"]
     say(f"[plan] main: {info}, busiest / mean = {info['max_load'] / mean:.4f}")
     assert info["max_load"] / mean < 1.01
-    assert info["partial_slots"] <= 2 * info["workgroups"]
+    # parts of rows cut between an XCD's workgroups, and of the shared tail
+    assert info["partial_slots"] <= 5 * info["workgroups"]
 
 
 # Every output row of the main, dense and tile-aligned (256 x 128) workloads
