@@ -38,12 +38,12 @@ void plan_persistent(const int32_t* steps, const float* weight, int32_t n_units,
   const double total = pre[M];
 
   // The shared tail: the last units, whose cost is at most `tail` of the
-  // total (at most P units), kept when there are four units per workgroup.
-  // The XCDs share units [0, Mx) as below.
+  // total, kept when there are four units per workgroup. The XCDs share
+  // units [0, Mx) as below.
   int64_t Mx = M;
   if (tail > 0.0 && M >= 4 * (int64_t)P) {
     const double want = tail * total;
-    while (Mx > 0 && M - Mx < P && pre[M] - pre[Mx - 1] <= want) --Mx;
+    while (Mx > 0 && pre[M] - pre[Mx - 1] <= want) --Mx;
   }
   const double xtotal = pre[Mx];
 

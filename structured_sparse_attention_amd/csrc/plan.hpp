@@ -82,8 +82,8 @@ struct PlanResult {
 // starting an item, in steps. min_part: a unit is not cut into parts of
 // fewer steps than this where it can be avoided. tail: the share of the
 // total cost kept for the shared tail (0: none); a tail is kept only when
-// there are at least four units per workgroup, and holds at most n_wg units
-// and kPlanTailSlotsPerWg * n_wg parts.
+// there are at least four units per workgroup, and its parts use at most
+// kPlanTailSlotsPerWg * n_wg partial slots.
 void plan_persistent(const int32_t* steps, const float* weight, int32_t n_units, int32_t n_wg,
                      int32_t n_xcd, int32_t block, int32_t overhead, int32_t min_part,
                      double tail, PlanResult& out);

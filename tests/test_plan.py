@@ -101,7 +101,7 @@ def check_plan(steps, plan, n_wg, overhead=4, weights=None):
         assert sorted(plan["queue"][qp[x]:qp[x + 1]]) == sorted(mine), x
     # tail units are whole in the tail, and cut into parts of falling size
     assert not tail_units & {it[0] for it in plan["queue"][:qp[X]]}
-    assert len(tail_units) <= P
+    assert sum(1 for it in plan["queue"][qp[X]:qp[X + 1]] if it[3] >= 0) <= 3 * P
     return load
 
 
