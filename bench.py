@@ -199,9 +199,10 @@ def cpu_baseline(w, Q, K, V, rows_per_head):
 # ------------------------------------------------------------------ routing
 
 def routing_times(w, host):
-    """Wall time of svg_route_heads (synchronous: scratch allocation, V^T,
-    partial and combine kernels, copy-back) on the original-order inputs, at
-    64 sampled rows and at 1% of the tokens."""
+    """Wall time of svg_route_heads (synchronous: V^T, partial and combine
+    kernels, copy-back; the untimed first call allocates the scratch that
+    later calls reuse) on the original-order inputs, at 64 sampled rows and
+    at 1% of the tokens."""
     import torch
     import seeded_inputs as si
     import structured_sparse_attention_amd as svg

@@ -282,10 +282,13 @@ svg_status svg_autotune_tiles(const svg_mask_spec* spec, const void* q,
  *   err:    host float [num_heads][2] (spatial, temporal error), or NULL.
  *   kinds:  host int32 [num_heads].
  * The scores use bf16 inputs and fp32 accumulation; P is rounded to bf16
- * for the PV product, as in svg_attn_fwd. Allocates one device scratch
- * (V^T of every head, num_heads*head_dim*(N+128)*2 bytes at most, plus
- * per-split partial results of about 1.6 KB per sampled row, head and
- * split), freed before return.
+ * for the PV product, as in svg_attn_fwd. Uses one device scratch (V^T of
+ * every head, num_heads*head_dim*(N+128)*2 bytes at most, plus per-split
+ * partial results of about 1.6 KB per sampled row, head and split; about
+ * 240 MB for 75,600 tokens, 10 heads, d = 128 and 756 rows), allocated on
+ * the first call that needs it and kept per device, the largest so far,
+ * until the process ends. Calls take a lock for their whole duration, so
+ * calls from several host threads run one after another.
  * Synchronous: returns after the results are on the host.
  * Errors: INVALID_ARG, UNSUPPORTED (head_dim), ALIGNMENT, OOM, HIP. */
 svg_status svg_route_heads(const svg_mask_spec* spec, const void* q,

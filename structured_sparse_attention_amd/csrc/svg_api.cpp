@@ -287,6 +287,17 @@ void order_rows(const int32_t* rows, int32_t n, int32_t S, int32_t* out) {
 std::mutex g_noalloc_mu;
 int32_t g_noalloc_rows[65536];
 
+// svg_route_heads keeps its scratch between calls, per device (the largest
+// so far): allocating and freeing a few hundred MB took about half of a
+// call's time. The calls are synchronous and hold the lock throughout, so
+// a scratch is never in use when it is replaced.
+std::mutex g_route_mu;
+struct RouteScratch {
+  char* p = nullptr;
+  int64_t bytes = 0;
+};
+std::vector<RouteScratch> g_route_scratch;  // by device
+
 }  // namespace
 
 extern "C" {
@@ -745,10 +756,27 @@ svg_status svg_route_heads(const svg_mask_spec* spec, const void* q, const void*
   const svg::RouteLayout L =
       svg::route_layout(ra.N, H, head_dim, n_rows, svg::route_slots(head_dim));
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  char* scratch = nullptr;
-  hipError_t e = hipMalloc(reinterpret_cast<void**>(&scratch), (size_t)L.bytes);
-  if (e != hipSuccess) return fail(SVG_ERR_OOM, "routing scratch of %lld bytes: %s",
-                                   (long long)L.bytes, hipGetErrorString(e));
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_route_mu);
+  if ((int)g_route_scratch.size() <= dev) g_route_scratch.resize(dev + 1);
+  RouteScratch& rs = g_route_scratch[dev];
+  if (rs.bytes < L.bytes) {
+    if (rs.p) {
+      e = hipFree(rs.p);
+      rs = RouteScratch{};
+      if (e != hipSuccess) return hip_fail(e, "hipFree");
+    }
+    e = hipMalloc(reinterpret_cast<void**>(&rs.p), (size_t)L.bytes);
+    if (e != hipSuccess) {
+      rs = RouteScratch{};
+      return fail(SVG_ERR_OOM, "routing scratch of %lld bytes: %s", (long long)L.bytes,
+                  hipGetErrorString(e));
+    }
+    rs.bytes = L.bytes;
+  }
+  char* scratch = rs.p;
   std::vector<float> err_h((size_t)H * 2);
   std::vector<int32_t> ordered((size_t)n_rows);
   order_rows(rows, n_rows, ra.S, ordered.data());
@@ -763,9 +791,7 @@ svg_status svg_route_heads(const svg_mask_spec* spec, const void* q, const void*
   if (e == hipSuccess)
     e = hipMemcpyAsync(kinds, scratch + L.kind_off, (size_t)H * 4, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
-  const hipError_t fe = hipFree(scratch);
   if (e != hipSuccess) return hip_fail(e, "routing kernels");
-  if (fe != hipSuccess) return hip_fail(fe, "hipFree");
   if (err) std::memcpy(err, err_h.data(), err_h.size() * 4);
   return ok();
 }
