@@ -142,7 +142,7 @@ def test_main_like_plan_is_exact_and_level(planner, block, weighted, tail):
     assert plan["n_slots"] > 0
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_plans_cover_every_step_once(planner, seed):
     rng = np.random.default_rng(seed)
     n_wg = int(rng.choice([1, 3, 8, 13, 64, 256, 304]))
@@ -156,7 +156,7 @@ def test_random_plans_cover_every_step_once(planner, seed):
     weights = rng.uniform(0.5, 2.0, size=n) if seed % 2 else None
     plan = planner(steps, n_wg=n_wg, n_xcd=n_xcd, overhead=overhead,
                    min_part=int(rng.choice([1, 16, 32])), block=block, weights=weights,
-                   tail=float(rng.choice([0.0, 0.05, 0.3])))
+                   tail=float(rng.choice([0.0, 0.05, 0.3, 1.0])))
     check_plan(list(steps), plan, n_wg, overhead=overhead, weights=weights)
 
 
