@@ -49,7 +49,7 @@ bool tile_q_ok(int32_t bq) {
 bool tile_k_ok(int32_t bk) { return bk >= 32 && bk <= 1024 && bk % 32 == 0; }
 
 void free_buffers(svg::MapBuffers& b) {
-  void* ptrs[] = {b.kinds, b.classes, b.rowinfo, b.row_ptr, b.entries, b.rowstats, b.stats};
+  void* ptrs[] = {b.kinds, b.classes, b.rowinfo, b.entries, b.rowstats};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   b = svg::MapBuffers{};
@@ -104,18 +104,11 @@ void plan_host_fn(void* user) {
   int32_t* ptr = im + 4;
   svg::ItemDesc* items = reinterpret_cast<svg::ItemDesc*>(im + pl.items_off());
   int32_t* comb = im + pl.combine_off();
-  // Each row's first schedule entry, as the device's exclusive scan places
-  // it, into the row info's unused field 6 (staging only; the device copy
-  // is not touched).
+  // Each row's first schedule entry (row r's entries start at r * nK) into
+  // the row info's unused field 6 (staging only; the device copy is not
+  // touched). R * nK fits int32: the build checks the capacity.
   const int64_t R = (int64_t)g.H * g.nQ;
-  {
-    int64_t acc = 0;
-    for (int64_t r = 0; r < R; ++r) {
-      int32_t* ri = j.rowinfo_host + r * svg::kRowInfo;
-      ri[6] = (int32_t)acc;
-      acc += ri[0] + ri[1];
-    }
-  }
+  for (int64_t r = 0; r < R; ++r) j.rowinfo_host[r * svg::kRowInfo + 6] = (int32_t)(r * g.nK);
   auto desc = [&](int32_t unit, int32_t s0, int32_t s1, int32_t slot) {
     const int32_t row = unit / j.nsub, sub = unit - row * j.nsub;
     const int32_t* ri = j.rowinfo_host + (int64_t)row * svg::kRowInfo;
@@ -404,10 +397,8 @@ svg_status svg_build_tile_map(const svg_mask_spec* spec, int32_t tile_q, int32_t
   step(alloc(&b.kinds, g.H));
   step(alloc(&b.classes, R * g.nK));
   step(alloc(&b.rowinfo, R * svg::kRowInfo));
-  step(alloc(&b.row_ptr, R + 1));
   step(alloc(&b.entries, b.capacity));
   step(alloc(&b.rowstats, R * svg::kRowStats));
-  step(alloc(&b.stats, (int64_t)g.H * svg::kRowStats));
   step(alloc(&pl.dev, pl.dev_ints()));
   step(alloc(&pl.counters, (int64_t)svg::kQueueRing * (pl.n_xcd + 1)));
   step(alloc(&pl.part_o, part_rows * svg::kAttnMaxHeadDim));
@@ -511,13 +502,19 @@ svg_status svg_tile_map_stats(const svg_tile_map* map, svg_head_stats* per_head,
     return fail(SVG_ERR_SHAPE_MISMATCH, "num_heads %d, map has %d", num_heads, map->geom.H);
   svg_status s = wait_built(map);
   if (s != SVG_OK) return s;
-  std::vector<int64_t> host((size_t)num_heads * svg::kRowStats);
-  const hipError_t e = hipMemcpy(host.data(), map->buf.stats, host.size() * sizeof(int64_t),
+  // the per-row statistics, summed per head here
+  const svg::MapGeometry& g = map->geom;
+  std::vector<int64_t> rows((size_t)num_heads * g.nQ * svg::kRowStats);
+  const hipError_t e = hipMemcpy(rows.data(), map->buf.rowstats, rows.size() * sizeof(int64_t),
                                  hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "copy of tile-map stats");
   for (int32_t h = 0; h < num_heads; ++h) {
-    const int64_t* r = host.data() + (size_t)h * svg::kRowStats;
-    per_head[h] = svg_head_stats{r[0], r[1], r[2], r[3], r[4], r[5], r[6], r[7]};
+    int64_t a[svg::kRowStats] = {};
+    for (int64_t qt = 0; qt < g.nQ; ++qt) {
+      const int64_t* r = rows.data() + ((size_t)h * g.nQ + qt) * svg::kRowStats;
+      for (int i = 0; i < svg::kRowStats; ++i) a[i] += r[i];
+    }
+    per_head[h] = svg_head_stats{a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7]};
   }
   return ok();
 }
@@ -542,31 +539,33 @@ svg_status svg_tile_map_copy_schedule(const svg_tile_map* map, int32_t* row_ptr,
   if (s != SVG_OK) return s;
   const svg::MapGeometry& g = map->geom;
   const size_t R = (size_t)g.H * g.nQ;
-  std::vector<int32_t> rp(R + 1);
-  hipError_t e = hipMemcpy(rp.data(), map->buf.row_ptr, (R + 1) * sizeof(int32_t),
+  // row r's executed tiles are its FULL and BOUNDARY counts (row info 0, 1);
+  // on the device its entries start at r * nK, packed here
+  std::vector<int32_t> ri(R * svg::kRowInfo);
+  hipError_t e = hipMemcpy(ri.data(), map->buf.rowinfo, ri.size() * sizeof(int32_t),
                            hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return hip_fail(e, "copy of row_ptr");
+  if (e != hipSuccess) return hip_fail(e, "copy of row info");
+  std::vector<int32_t> rp(R + 1, 0);
+  for (size_t r = 0; r < R; ++r)
+    rp[r + 1] = rp[r] + ri[r * svg::kRowInfo + 0] + ri[r * svg::kRowInfo + 1];
   if (entries && n_entries < (size_t)rp[R])
     return fail(SVG_ERR_SHAPE_MISMATCH, "n_entries = %zu, schedule has %d entries", n_entries,
                 rp[R]);
   if (row_ptr) std::memcpy(row_ptr, rp.data(), (R + 1) * sizeof(int32_t));
-  if (n_full || sink_ab) {
-    std::vector<int32_t> ri(R * svg::kRowInfo);
-    e = hipMemcpy(ri.data(), map->buf.rowinfo, ri.size() * sizeof(int32_t),
-                  hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return hip_fail(e, "copy of row info");
-    for (size_t r = 0; r < R; ++r) {
-      if (n_full) n_full[r] = ri[r * svg::kRowInfo + 0];
-      if (sink_ab) {
-        sink_ab[2 * r] = ri[r * svg::kRowInfo + 2];
-        sink_ab[2 * r + 1] = ri[r * svg::kRowInfo + 3];
-      }
+  for (size_t r = 0; r < R; ++r) {
+    if (n_full) n_full[r] = ri[r * svg::kRowInfo + 0];
+    if (sink_ab) {
+      sink_ab[2 * r] = ri[r * svg::kRowInfo + 2];
+      sink_ab[2 * r + 1] = ri[r * svg::kRowInfo + 3];
     }
   }
   if (entries && rp[R] > 0) {
-    e = hipMemcpy(entries, map->buf.entries, (size_t)rp[R] * sizeof(int32_t),
+    std::vector<int32_t> all(R * (size_t)g.nK);
+    e = hipMemcpy(all.data(), map->buf.entries, all.size() * sizeof(int32_t),
                   hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "copy of schedule entries");
+    for (size_t r = 0; r < R; ++r)
+      std::memcpy(entries + rp[r], all.data() + r * g.nK, (size_t)(rp[r + 1] - rp[r]) * 4);
   }
   return ok();
 }

@@ -30,11 +30,9 @@ struct MapBuffers {
   int32_t* kinds = nullptr;     // [H]
   uint8_t* classes = nullptr;   // [H][nQ][nK]
   int32_t* rowinfo = nullptr;   // [H*nQ][kRowInfo]
-  int32_t* row_ptr = nullptr;   // [H*nQ + 1]
-  int32_t* entries = nullptr;   // [capacity]
+  int32_t* entries = nullptr;   // [H*nQ][nK]: row r's entries start at r * nK
   int64_t* rowstats = nullptr;  // [H*nQ][kRowStats]
-  int64_t* stats = nullptr;     // [H][kRowStats]
-  int64_t capacity = 0;
+  int64_t capacity = 0;         // H*nQ*nK
 };
 
 // Write the head kinds (host array [H], values 0..2) to device memory from
@@ -42,7 +40,7 @@ struct MapBuffers {
 hipError_t launch_set_kinds(const int32_t* host_kinds, int32_t H, int32_t* dev_kinds,
                             hipStream_t stream);
 
-// Launch the tile-map kernels (classify, scan, compact, per-head stats).
+// Launch the tile-map kernel (classify and compact every row).
 hipError_t launch_build_tile_map(const MapGeometry& g, const MapBuffers& b,
                                  hipStream_t stream);
 

@@ -88,6 +88,36 @@ __device__ void block_sum(int64_t (&v)[N], int64_t* lds) {
   }
 }
 
+// Ordered compaction of one row's classes in [lo, hi] (all threads of the
+// block): FULL ids ascending, then BOUNDARY ids ascending.
+__device__ void compact_row(const uint8_t* cls_row, int lo, int hi, int32_t* out) {
+  __shared__ int wave_tot[kThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int pos = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const uint8_t want = pass == 0 ? SVG_TILE_FULL : SVG_TILE_BOUNDARY;
+    for (int c = lo; c <= hi; c += kThreads) {
+      const int kt = c + threadIdx.x;
+      const bool flag = kt <= hi && cls_row[kt] == want;
+      const uint64_t m = __ballot(flag);
+      const int before = __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == 0) wave_tot[wave] = __popcll(m);
+      __syncthreads();
+      int off = 0, tot = 0;
+      for (int w = 0; w < kThreads / 64; ++w) {
+        off += w < wave ? wave_tot[w] : 0;
+        tot += wave_tot[w];
+      }
+      if (flag) out[pos + off + before] = kt;
+      pos += tot;
+      __syncthreads();
+    }
+  }
+}
+
+// Classification of one row of tiles, then the row's compaction: FULL ids of
+// the run range ascending, then BOUNDARY ids ascending, into the row's own
+// nK entries (entries[row * nK ...]), so that no scan across rows is needed.
 __global__ __launch_bounds__(kThreads) void classify_kernel(MapGeometry g, MapBuffers b) {
   const int qt = blockIdx.x, h = blockIdx.y;
   const int64_t row = (int64_t)h * g.nQ + qt;
@@ -149,6 +179,9 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MapGeometry g, MapBu
   }
   __shared__ int64_t lds[kThreads / 64 * 6];
   block_sum(acc, lds);
+  // (the barrier in block_sum follows every thread's class bytes, so the
+  // whole block sees them)
+  compact_row(cls_row, (int)lo, (int)hi, b.entries + row * g.nK);
   if (threadIdx.x == 0) {
     int32_t* ri = b.rowinfo + row * kRowInfo;
     ri[0] = (int32_t)acc[3];
@@ -171,64 +204,6 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MapGeometry g, MapBu
   }
 }
 
-// Exclusive scan of executed tiles per row -> row_ptr (one block).
-__global__ __launch_bounds__(1024) void scan_kernel(int64_t R, const int32_t* rowinfo,
-                                                    int32_t* row_ptr) {
-  __shared__ int64_t part[1024];
-  const int t = threadIdx.x;
-  const int64_t per = (R + 1023) / 1024;
-  const int64_t r0 = t * per, r1 = min(R, r0 + per);
-  int64_t s = 0;
-  for (int64_t r = r0; r < r1; ++r) s += rowinfo[r * kRowInfo] + rowinfo[r * kRowInfo + 1];
-  part[t] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int64_t x = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += x;
-    __syncthreads();
-  }
-  int64_t base = part[t] - s;  // exclusive
-  for (int64_t r = r0; r < r1; ++r) {
-    row_ptr[r] = (int32_t)base;
-    base += rowinfo[r * kRowInfo] + rowinfo[r * kRowInfo + 1];
-  }
-  if (t == 1023) row_ptr[R] = (int32_t)part[1023];
-}
-
-// Ordered compaction of one row: FULL ids of the run range ascending, then
-// BOUNDARY ids ascending.
-__global__ __launch_bounds__(kThreads) void compact_kernel(MapGeometry g, MapBuffers b) {
-  const int qt = blockIdx.x, h = blockIdx.y;
-  const int64_t row = (int64_t)h * g.nQ + qt;
-  const int32_t* ri = b.rowinfo + row * kRowInfo;
-  const int lo = ri[4], hi = ri[5];
-  const uint8_t* cls_row = b.classes + row * g.nK;
-  int32_t* out = b.entries + b.row_ptr[row];
-  __shared__ int wave_tot[kThreads / 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int pos = 0;
-  for (int pass = 0; pass < 2; ++pass) {
-    const uint8_t want = pass == 0 ? SVG_TILE_FULL : SVG_TILE_BOUNDARY;
-    for (int c = lo; c <= hi; c += kThreads) {
-      const int kt = c + threadIdx.x;
-      const bool flag = kt <= hi && cls_row[kt] == want;
-      const uint64_t m = __ballot(flag);
-      const int before = __popcll(m & ((1ull << lane) - 1ull));
-      if (lane == 0) wave_tot[wave] = __popcll(m);
-      __syncthreads();
-      int off = 0, tot = 0;
-      for (int w = 0; w < kThreads / 64; ++w) {
-        off += w < wave ? wave_tot[w] : 0;
-        tot += wave_tot[w];
-      }
-      if (flag) out[pos + off + before] = kt;
-      pos += tot;
-      __syncthreads();
-    }
-  }
-}
-
 // Head kinds of up to kKindChunk heads, carried in the kernel arguments so
 // that the build needs neither a host-to-device copy nor a wait for one.
 constexpr int kKindChunk = 256;
@@ -238,22 +213,6 @@ struct KindChunk {
 };
 __global__ __launch_bounds__(kKindChunk) void set_kinds_kernel(KindChunk c, int32_t* kinds) {
   if ((int)threadIdx.x < c.n) kinds[c.h0 + threadIdx.x] = c.kind[threadIdx.x];
-}
-
-__global__ __launch_bounds__(kThreads) void stats_kernel(MapGeometry g, MapBuffers b) {
-  const int h = blockIdx.x;
-  int64_t acc[kRowStats] = {};
-  for (int64_t qt = threadIdx.x; qt < g.nQ; qt += kThreads) {
-    const int64_t* rs = b.rowstats + ((int64_t)h * g.nQ + qt) * kRowStats;
-#pragma unroll
-    for (int i = 0; i < kRowStats; ++i) acc[i] += rs[i];
-  }
-  __shared__ int64_t lds[kThreads / 64 * kRowStats];
-  block_sum(acc, lds);
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int i = 0; i < kRowStats; ++i) b.stats[h * kRowStats + i] = acc[i];
-  }
 }
 
 }  // namespace
@@ -276,14 +235,6 @@ hipError_t launch_build_tile_map(const MapGeometry& g, const MapBuffers& b,
                                  hipStream_t stream) {
   const dim3 rows_grid(g.nQ, g.H);
   hipLaunchKernelGGL(classify_kernel, rows_grid, dim3(kThreads), 0, stream, g, b);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream,
-                     (int64_t)g.H * g.nQ, (const int32_t*)b.rowinfo, b.row_ptr);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(compact_kernel, rows_grid, dim3(kThreads), 0, stream, g, b);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(stats_kernel, dim3(g.H), dim3(kThreads), 0, stream, g, b);
   return hipGetLastError();
 }
 
