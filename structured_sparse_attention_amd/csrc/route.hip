@@ -40,6 +40,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 namespace svg {
 namespace {
@@ -230,7 +231,8 @@ __global__ __launch_bounds__(RW * 64) void route_partial(RouteParams p) {
   constexpr float NEG_INF = -__builtin_huge_valf();
   __shared__ __attribute__((aligned(16))) char lds[2 * STB];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, n = lane & 15, g4 = 4 * g;
   const int split = blockIdx.x, h = blockIdx.z;
   const int rb = blockIdx.y * RW + wave;  // block of 16 sampled rows
@@ -266,12 +268,15 @@ __global__ __launch_bounds__(RW * 64) void route_partial(RouteParams p) {
   uint4 pre0, pre1, pre2, pre3;  // separate values: an array here would live in scratch
   auto fetch1 = [&](int key0, int j, uint4& r) __attribute__((always_inline)) {
     const int c = tid + j * NT;
+    // uniform base + 32-bit lane offset (one head's K and V^T stay below
+    // 2 GiB): no 64-bit address per lane has to stay live across the loop
     if (j < NKCH / NT) {
       const int key = min(key0 + c / KCH, p.N - 1);
-      r = *(const uint4*)(kh + (size_t)key * D + 8 * (c % KCH));
+      r = *(const uint4*)((const char*)kh + (uint32_t)(key * (2 * D) + 16 * (c % KCH)));
     } else {
       const int cv = c - NKCH;
-      r = *(const uint4*)(vth + (size_t)(cv >> 3) * p.pitch + key0 + 8 * (cv & 7));
+      r = *(const uint4*)((const char*)(vth + key0) +
+                          (uint32_t)(2 * ((cv >> 3) * p.pitch + 8 * (cv & 7))));
     }
   };
   auto store1 = [&](char* buf, int j, const uint4& r) __attribute__((always_inline)) {
@@ -407,9 +412,16 @@ __global__ __launch_bounds__(RW * 64) void route_partial(RouteParams p) {
           lx += sx;
         }
       };
+      // A mask that keeps none of the step's keys for any row of the wave
+      // adds nothing to its output: its weights and MFMAs are skipped (the
+      // sums with zero weights are the same values).
       uint32_t ps[8], pt[8];
-      masked(lane_keep(p, 1, fq, sq, key0, fk0, sk0, g4, sq_lo, sq_hi), ps, ls);
-      masked(lane_keep(p, 2, fq, sq, key0, fk0, sk0, g4, sq_lo, sq_hi), pt, lt);
+      const uint32_t lks = lane_keep(p, 1, fq, sq, key0, fk0, sk0, g4, sq_lo, sq_hi);
+      const bool any_s = __builtin_amdgcn_ballot_w64(lks != 0u) != 0;
+      if (any_s) masked(lks, ps, ls);
+      const uint32_t lkt = lane_keep(p, 2, fq, sq, key0, fk0, sk0, g4, sq_lo, sq_hi);
+      const bool any_t = __builtin_amdgcn_ballot_w64(lkt != 0u) != 0;
+      if (any_t) masked(lkt, pt, lt);
       // O^T += V^T P^T: V^T of dims 16db + n, positions 32c2 + 8g .. +7
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
@@ -426,10 +438,17 @@ __global__ __launch_bounds__(RW * 64) void route_partial(RouteParams p) {
             vb[db] = *(const bf16x8*)(buf + KBYTES + (16 * db + n) * VROWB + 64 + 16 * g);
         }
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NDB; ++db)
           od[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], bd, od[db], 0, 0, 0);
-          os[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], bs, os[db], 0, 0, 0);
-          ot[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], bt, ot[db], 0, 0, 0);
+        if (any_s) {
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            os[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], bs, os[db], 0, 0, 0);
+        }
+        if (any_t) {
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            ot[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], bt, ot[db], 0, 0, 0);
         }
         if (c2 == 0) {
 #pragma unroll
@@ -454,9 +473,13 @@ __global__ __launch_bounds__(RW * 64) void route_partial(RouteParams p) {
   ld = row_sum4(ld);
   ls = row_sum4(ls);
   lt = row_sum4(lt);
-  if (!rvalid) return;
-  float* out = p.part + (((size_t)h * p.n_rows + ri) * p.n_split + split) * 3 * (D + 2);
-  if (g == 0) {
+  // The lane's row and group again, from the lane count: kept live across
+  // the loop they would take registers the loop needs.
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int ge = lane_e >> 4, ri_e = rb * RQ + (lane_e & 15);
+  if (ri_e >= p.n_rows) return;
+  float* out = p.part + (((size_t)h * p.n_rows + ri_e) * p.n_split + split) * 3 * (D + 2);
+  if (ge == 0) {
     out[0] = m;
     out[1] = ld;
     out[D + 2] = m;
@@ -468,7 +491,7 @@ __global__ __launch_bounds__(RW * 64) void route_partial(RouteParams p) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int d = 2 + 16 * db + g4 + i;
+      const int d = 2 + 16 * db + 4 * ge + i;
       out[d] = od[db][i];
       out[D + 2 + d] = os[db][i];
       out[2 * (D + 2) + d] = ot[db][i];
