@@ -549,24 +549,53 @@ __device__ float exact_output(const RouteParams& p, int h, int t, int x, float* 
 }
 
 // One workgroup of D threads per (sampled row, head): merges the splits of
-// the three outputs; writes the row's two squared-error sums (float64).
+// the three outputs; writes the row's two squared-error sums (float64). The
+// splits' maxima and sums are spread over the threads and reduced in LDS;
+// each thread then sums its output column over the splits in order, with
+// the weights of D splits at a time staged in LDS, so that the column's
+// loads are independent of each other and can be in flight together.
 template <int D>
 __global__ __launch_bounds__(D) void route_rows(RouteParams p, double* row_err) {
   const int ri = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
   const float* base = p.part + ((size_t)h * p.n_rows + ri) * p.n_split * 3 * (D + 2);
   __shared__ float sh[2 * D];
+  __shared__ float wsh[D], rsh[D];
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  // max (take_max) or sum over the block; every thread gets the same value
+  auto reduce = [&](float v, bool take_max) {
+    rsh[d] = v;
+    __syncthreads();
+    for (int w = D / 2; w > 0; w >>= 1) {
+      if (d < w) rsh[d] = take_max ? fmaxf(rsh[d], rsh[d + w]) : rsh[d] + rsh[d + w];
+      __syncthreads();
+    }
+    const float r = rsh[0];
+    __syncthreads();
+    return r;
+  };
   float out[3];
 #pragma unroll
   for (int x = 0; x < 3; ++x) {
-    float M = -__builtin_huge_valf();
-    for (int sp = 0; sp < p.n_split; ++sp) M = fmaxf(M, base[(sp * 3 + x) * (D + 2)]);
-    float L = 0.f, A = 0.f;
-    for (int sp = 0; sp < p.n_split; ++sp) {
-      const float* b = base + (sp * 3 + x) * (D + 2);
-      const float w = b[0] == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(b[0] - M);
-      L += b[1] * w;
-      A += b[2 + d] * w;
+    float mx = NEG_INF;
+    for (int sp = d; sp < p.n_split; sp += D) mx = fmaxf(mx, base[(sp * 3 + x) * (D + 2)]);
+    const float M = reduce(mx, true);
+    float Lp = 0.f, A = 0.f;
+    for (int c0 = 0; c0 < p.n_split; c0 += D) {
+      float w = 0.f;
+      if (c0 + d < p.n_split) {
+        const float* b = base + ((c0 + d) * 3 + x) * (D + 2);
+        w = b[0] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(b[0] - M);
+        Lp += b[1] * w;
+      }
+      wsh[d] = w;
+      __syncthreads();
+      const int cnt = min(D, p.n_split - c0);
+      const float* a = base + (c0 * 3 + x) * (D + 2) + 2 + d;
+#pragma unroll 8
+      for (int j = 0; j < cnt; ++j) A += a[(size_t)j * 3 * (D + 2)] * wsh[j];
+      __syncthreads();
     }
+    const float L = reduce(Lp, false);
     // every thread holds the same L: the branch is uniform
     if (x > 0 && !(L >= kExactBelow)) out[x] = exact_output<D>(p, h, p.rows[ri], x, sh);
     else out[x] = L > 0.f ? A / L : 0.f;
