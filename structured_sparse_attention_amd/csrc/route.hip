@@ -550,55 +550,74 @@ __device__ float exact_output(const RouteParams& p, int h, int t, int x, float* 
 
 // One workgroup of D threads per (sampled row, head): merges the splits of
 // the three outputs; writes the row's two squared-error sums (float64). The
-// splits' maxima and sums are spread over the threads and reduced in LDS;
-// each thread then sums its output column over the splits in order, with
-// the weights of D splits at a time staged in LDS, so that the column's
-// loads are independent of each other and can be in flight together.
+// splits' maxima and sums are spread over the threads and reduced within
+// each wave, then across the waves through LDS; each thread then sums its
+// output column over the splits in order, with the weights of D splits at a
+// time staged in LDS, so that the column's loads are independent of each
+// other and can be in flight together.
 template <int D>
 __global__ __launch_bounds__(D) void route_rows(RouteParams p, double* row_err) {
+  constexpr int NWV = D / 64;  // waves
   const int ri = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
   const float* base = p.part + ((size_t)h * p.n_rows + ri) * p.n_split * 3 * (D + 2);
   __shared__ float sh[2 * D];
-  __shared__ float wsh[D], rsh[D];
+  __shared__ float wsh[3][D], rsh[3][NWV];
   constexpr float NEG_INF = -__builtin_huge_valf();
-  // max (take_max) or sum over the block; every thread gets the same value
-  auto reduce = [&](float v, bool take_max) {
-    rsh[d] = v;
-    __syncthreads();
-    for (int w = D / 2; w > 0; w >>= 1) {
-      if (d < w) rsh[d] = take_max ? fmaxf(rsh[d], rsh[d + w]) : rsh[d] + rsh[d + w];
-      __syncthreads();
-    }
-    const float r = rsh[0];
-    __syncthreads();
-    return r;
-  };
-  float out[3];
+  // the three values' maxima (take_max) or sums over the block; every thread
+  // gets the same results
+  auto reduce3 = [&](float (&v)[3], bool take_max) __attribute__((always_inline)) {
 #pragma unroll
-  for (int x = 0; x < 3; ++x) {
-    float mx = NEG_INF;
-    for (int sp = d; sp < p.n_split; sp += D) mx = fmaxf(mx, base[(sp * 3 + x) * (D + 2)]);
-    const float M = reduce(mx, true);
-    float Lp = 0.f, A = 0.f;
-    for (int c0 = 0; c0 < p.n_split; c0 += D) {
+    for (int x = 0; x < 3; ++x) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float u = __shfl_xor(v[x], o);
+        v[x] = take_max ? fmaxf(v[x], u) : v[x] + u;
+      }
+      if ((d & 63) == 0) rsh[x][d >> 6] = v[x];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      v[x] = rsh[x][0];
+#pragma unroll
+      for (int i = 1; i < NWV; ++i) v[x] = take_max ? fmaxf(v[x], rsh[x][i]) : v[x] + rsh[x][i];
+    }
+    __syncthreads();
+  };
+  float M[3] = {NEG_INF, NEG_INF, NEG_INF};
+  for (int sp = d; sp < p.n_split; sp += D)
+#pragma unroll
+    for (int x = 0; x < 3; ++x) M[x] = fmaxf(M[x], base[(sp * 3 + x) * (D + 2)]);
+  reduce3(M, true);
+  float L[3] = {0.f, 0.f, 0.f}, A[3] = {0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < p.n_split; c0 += D) {
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
       float w = 0.f;
       if (c0 + d < p.n_split) {
         const float* b = base + ((c0 + d) * 3 + x) * (D + 2);
-        w = b[0] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(b[0] - M);
-        Lp += b[1] * w;
+        w = b[0] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(b[0] - M[x]);
+        L[x] += b[1] * w;
       }
-      wsh[d] = w;
-      __syncthreads();
-      const int cnt = min(D, p.n_split - c0);
+      wsh[x][d] = w;
+    }
+    __syncthreads();
+    const int cnt = min(D, p.n_split - c0);
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
       const float* a = base + (c0 * 3 + x) * (D + 2) + 2 + d;
 #pragma unroll 8
-      for (int j = 0; j < cnt; ++j) A += a[(size_t)j * 3 * (D + 2)] * wsh[j];
-      __syncthreads();
+      for (int j = 0; j < cnt; ++j) A[x] += a[(size_t)j * 3 * (D + 2)] * wsh[x][j];
     }
-    const float L = reduce(Lp, false);
+    __syncthreads();
+  }
+  reduce3(L, false);
+  float out[3];
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
     // every thread holds the same L: the branch is uniform
-    if (x > 0 && !(L >= kExactBelow)) out[x] = exact_output<D>(p, h, p.rows[ri], x, sh);
-    else out[x] = L > 0.f ? A / L : 0.f;
+    if (x > 0 && !(L[x] >= kExactBelow)) out[x] = exact_output<D>(p, h, p.rows[ri], x, sh);
+    else out[x] = L[x] > 0.f ? A[x] / L[x] : 0.f;
   }
   __shared__ double red[2][D];
   red[0][d] = (double)(out[1] - out[0]) * (double)(out[1] - out[0]);
