@@ -161,6 +161,19 @@ def test_routing_main_workload_sampled_rows():
     say(f"  kinds {kinds}, {decided} decided beyond the error bars")
 
 
+@pytest.mark.timeout(900)
+def test_routing_main_workload_one_percent_of_rows():
+    """The bench's larger routing case: 1% of the tokens (756 rows), six
+    128-row blocks per head, the last ragged, over a few long key splits."""
+    w = si.workload("main")
+    n = w.seq_len // 100
+    say(f"[route-main-1pct] N={w.seq_len} H={w.num_heads}: {n} sampled rows")
+    Q, K, V = si.draw_qkv(w)
+    rows = si.draw_query_subset(w, n, seed=77)
+    kinds, decided = _compare(w, Q, K, V, rows, "main-1pct")
+    say(f"  kinds {kinds}, {decided} decided beyond the error bars")
+
+
 def test_routing_rejects_bad_rows():
     w = si.workload("tiny")
     Q, K, V = si.draw_qkv(w)
